@@ -1,0 +1,136 @@
+"""fp64 CPU oracle for Gemma-4-31B decode attention (slidingDecodeGQA / decodeGQA).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, ``__graft_entry__.smoke()`` and
+the benchmark's ``cpu_baseline`` leg may import this package.  The HIP library
+never imports, links or calls it, and it imports nothing from the HIP side.
+
+The arithmetic lives in ``gqa_oracle.c`` (plain C, double precision); this
+module only compiles it with gcc and marshals numpy arrays into it.  It
+follows the attn.core rows of the "Compute-graph nodes" table of the
+gemma-4-31B Model Spec page and the tensor shapes of its "Tensors of the main
+nodes" table.
+
+Parity status of every function here: pinned by ``tests/test_oracle_pins.py``
+(brute-force masked softmax, torch SDPA in float64, closed forms, bit-exact
+selection, invariants and planted-mistake checks).  The only unpinned reading
+is the zero row for seq_len <= 0 ("parity unpinned": the pages' shape domain
+starts at S = 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "gqa_oracle.c")
+LIBRARY = os.path.join(_HERE, "libgqaoracle.so")
+
+HEADS = 32
+PAGE = 16
+F32, BF16 = 0, 1
+
+# variant -> (kv heads, head dim, window); attn.core rows of the Model Spec page
+VARIANTS = {
+    "sliding": (16, 256, 1024),
+    "global": (4, 512, 0),
+}
+
+_ERRORS = {-1: "bad argument", -2: "seq_len above capacity", -3: "page id outside pool",
+           -4: "out of memory"}
+
+
+def build(source: str = SOURCE, out: str = LIBRARY, extra=()) -> str:
+    """Compile the oracle with gcc (no fast-math) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           *extra, source, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_libs: dict = {}
+
+
+def load(path: str = LIBRARY):
+    """Load (building first if absent) an oracle shared library."""
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
+    if path == os.path.abspath(LIBRARY) and not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    fn = lib.oracle_gqa_decode
+    p = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    fn.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, i32,
+                   p, i32]
+    fn.restype = ctypes.c_int
+    _libs[path] = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # raw bfloat16 bit patterns
+        return BF16
+    raise TypeError(f"oracle takes float32 or uint16 (bf16 bits) arrays, got {a.dtype}")
+
+
+def gqa_decode(variant, q, k, v, seq_lens, block_table=None, num_pages=None, rows=None,
+               nthreads: int | None = None, window: int | None = None, lib=None) -> np.ndarray:
+    """Reference decode attention in fp64.
+
+    variant: "sliding" or "global" (or an explicit (KV, D, window) tuple).
+    q [B,32,D]; k, v [B,S,KV,D] (contiguous) or [num_pages,16,KV,D] (paged, with
+    block_table [B,max_pages] int32); seq_lens [B] int32.  q/k/v are float32
+    arrays or uint16 arrays holding bf16 bits.  ``window`` overrides the
+    variant's window (<= 0: none).  ``rows``: optional list of (b, h) pairs.
+    Returns float64 [B,32,D], or [len(rows), D] when rows is given.
+    """
+    KV, D, W = VARIANTS[variant] if isinstance(variant, str) else variant
+    if window is not None:
+        W = window
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share a dtype")
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = q.shape[0]
+    if q.shape != (B, HEADS, D) or seq_lens.shape != (B,):
+        raise ValueError("q must be [B,32,D] and seq_lens [B]")
+    if block_table is None:
+        if k.ndim != 4 or k.shape[0] != B or k.shape[2:] != (KV, D) or v.shape != k.shape:
+            raise ValueError("contiguous k/v must be [B,S,KV,D]")
+        cap, max_pages, n_pages, bt = k.shape[1], 0, 0, None
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B,max_pages]")
+        if k.ndim != 4 or k.shape[1:] != (PAGE, KV, D) or v.shape != k.shape:
+            raise ValueError("paged k/v must be [num_pages,16,KV,D]")
+        max_pages = bt.shape[1]
+        n_pages = k.shape[0] if num_pages is None else num_pages
+        cap = max_pages * PAGE
+    if rows is None:
+        rows_arr, n_rows = None, B * HEADS
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, D), dtype=np.float64)
+    nthreads = nthreads or min(os.cpu_count() or 1, 16)
+    rc = lib.oracle_gqa_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(bt), B, cap,
+                               max_pages, n_pages, KV, D, W, _ptr(rows_arr), n_rows, _ptr(out),
+                               nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
+    return out.reshape(B, HEADS, D) if rows is None else out

@@ -1,0 +1,210 @@
+/*
+ * gqa_oracle.c -- plain, slow, fp64 CPU oracle for Gemma-4-31B decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test-suite, the smoke check and the
+ * benchmark's cpu_baseline leg use it.  It shares no code, header, table or
+ * constant with the HIP library; it is the definition written out, nothing more.
+ *
+ * What it computes (the attn.core rows of the "Compute-graph nodes" table on
+ * the gemma-4-31B Model Spec page, docs.theformalera.com):
+ *
+ *   slidingDecodeGQA : o[b,h] = sum_s softmax_s(1 * <q[b,h], k[b,s,h/2]>) * v[b,s,h/2]
+ *                      over the last 1024 positions below seq_lens[b]
+ *   decodeGQA        : the same with k/v head h/8 and every position s < seq_lens[b]
+ *
+ * Tensor shapes follow the "Tensors of the main nodes" table of the same page:
+ * q [B,32,D], k/v [B,S,kv,D], seq_lens [B], o [B,32,D].  The paged form uses the
+ * page size 16 named in the "At a glance" table ("Shape domain" row).
+ *
+ * Readings where the pages leave a step open (each is also listed with the
+ * design notes):
+ *   - window: the query is the newest token, already appended to the cache
+ *     (compact forward pass of "Gemma 4 31B-it Text Architecture", which
+ *     appends K/V before attention and masks keys t-1024 < s <= t), so with
+ *     t = L-1 the window is [max(0, L-W), L);
+ *   - h/G is floor division (repeat_kv gives query heads G*j .. G*j+G-1 the
+ *     kv head j);
+ *   - scale is exactly 1 and no logit soft-cap applies to attention;
+ *   - L <= 0 yields a zero row (outside the shape domain S >= 1);
+ *   - paged pool layout [num_pages, 16, kv, D], logical position s lives in
+ *     physical page block_table[b][s/16], slot s%16.
+ *
+ * Arithmetic: every input element is widened exactly to double (bf16 by
+ * placing its 16 bits in the top half of an IEEE single), the dot products,
+ * the max, the exponentials, the normaliser and the weighted sum are all
+ * formed in double, in position order, with no blocking or reordering.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_HEADS 32
+#define ORC_PAGE 16
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum {
+  ORC_OK = 0,
+  ORC_ERR_ARG = -1,
+  ORC_ERR_SEQLEN = -2,
+  ORC_ERR_PAGE = -3,
+  ORC_ERR_NOMEM = -4
+};
+
+typedef struct {
+  int dtype;
+  const void *q, *k, *v;
+  const int32_t *seq_lens;
+  const int32_t *block_table; /* NULL: contiguous cache */
+  int32_t B, cap, max_pages, num_pages, KV, D, window;
+  const int32_t *rows; /* (b, h) pairs or NULL for every row */
+  int32_t n_rows;
+  double *out;
+  /* shared work counter and first error */
+  int32_t next;
+  int32_t err;
+  pthread_mutex_t mu;
+} orc_job;
+
+/* Exact widening of one stored element to double. */
+static double orc_elem(const void *base, int dtype, size_t idx) {
+  if (dtype == ORC_F32) return (double)((const float *)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Element offset of row (b, position s, kv head g) in k or v; -1 if the
+ * block table names a page outside the pool. */
+static int64_t orc_row_offset(const orc_job *j, int b, int64_t s, int g) {
+  if (j->block_table == NULL)
+    return (((int64_t)b * j->cap + s) * j->KV + g) * (int64_t)j->D;
+  int32_t page = j->block_table[(int64_t)b * j->max_pages + s / ORC_PAGE];
+  if (page < 0 || page >= j->num_pages) return -1;
+  return (((int64_t)page * ORC_PAGE + s % ORC_PAGE) * j->KV + g) * (int64_t)j->D;
+}
+
+/* One output row o[b,h,:] written to out[0:D]. */
+static int orc_one_row(const orc_job *j, int b, int h, double *out) {
+  const int D = j->D;
+  const int G = ORC_HEADS / j->KV; /* query heads per kv head */
+  const int g = h / G;             /* kv head of query head h */
+  const int64_t L = j->seq_lens[b];
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (L > j->cap) return ORC_ERR_SEQLEN;
+  if (L <= 0) return ORC_OK;
+  const int64_t lo = (j->window > 0 && L > j->window) ? L - j->window : 0;
+  const int64_t n = L - lo;
+
+  double *z = (double *)malloc((size_t)n * sizeof(double));
+  if (!z) return ORC_ERR_NOMEM;
+  const size_t qoff = ((size_t)b * ORC_HEADS + h) * (size_t)D;
+
+  /* logits z_s = 1 * <q[b,h], k[b,s,g]> */
+  for (int64_t s = lo; s < L; ++s) {
+    int64_t off = orc_row_offset(j, b, s, g);
+    if (off < 0) { free(z); return ORC_ERR_PAGE; }
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d)
+      acc += orc_elem(j->q, j->dtype, qoff + d) * orc_elem(j->k, j->dtype, (size_t)off + d);
+    z[s - lo] = acc;
+  }
+  /* softmax over the window */
+  double m = -INFINITY;
+  for (int64_t i = 0; i < n; ++i)
+    if (z[i] > m) m = z[i];
+  double l = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    z[i] = exp(z[i] - m);
+    l += z[i];
+  }
+  /* weighted sum of the value rows */
+  for (int64_t s = lo; s < L; ++s) {
+    int64_t off = orc_row_offset(j, b, s, g);
+    const double p = z[s - lo];
+    for (int d = 0; d < D; ++d) out[d] += p * orc_elem(j->v, j->dtype, (size_t)off + d);
+  }
+  for (int d = 0; d < D; ++d) out[d] /= l;
+  free(z);
+  return ORC_OK;
+}
+
+static void *orc_worker(void *arg) {
+  orc_job *j = (orc_job *)arg;
+  for (;;) {
+    pthread_mutex_lock(&j->mu);
+    int32_t r = j->next++;
+    int32_t bad = j->err;
+    pthread_mutex_unlock(&j->mu);
+    if (r >= j->n_rows || bad) break;
+    int b, h;
+    if (j->rows) {
+      b = j->rows[2 * r];
+      h = j->rows[2 * r + 1];
+    } else {
+      b = r / ORC_HEADS;
+      h = r % ORC_HEADS;
+    }
+    int rc = (b < 0 || b >= j->B || h < 0 || h >= ORC_HEADS)
+                 ? ORC_ERR_ARG
+                 : orc_one_row(j, b, h, j->out + (size_t)r * j->D);
+    if (rc) {
+      pthread_mutex_lock(&j->mu);
+      if (!j->err) j->err = rc;
+      pthread_mutex_unlock(&j->mu);
+    }
+  }
+  return NULL;
+}
+
+/*
+ * oracle_gqa_decode
+ *   dtype        ORC_F32 or ORC_BF16 (q, k, v share it)
+ *   q            [B, 32, D]
+ *   k, v         contiguous: [B, cap, KV, D]; paged: [num_pages, 16, KV, D]
+ *   seq_lens     [B] int32
+ *   block_table  NULL (contiguous) or [B, max_pages] int32 (paged; cap must
+ *                then equal max_pages*16)
+ *   KV, D        16/256 for slidingDecodeGQA, 4/512 for decodeGQA
+ *   window       1024 for slidingDecodeGQA, <= 0 for no window
+ *   rows         n_rows (b, h) pairs, or NULL for all B*32 rows in order
+ *   out          [n_rows, D] doubles
+ *   nthreads     worker threads (>= 1)
+ * Returns 0 or a negative ORC_ERR_* code.
+ */
+int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
+                      const int32_t *seq_lens, const int32_t *block_table, int32_t B,
+                      int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV,
+                      int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
+                      double *out, int32_t nthreads) {
+  if (!q || !k || !v || !seq_lens || !out) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (B < 1 || cap < 1 || KV < 1 || ORC_HEADS % KV != 0 || D < 1) return ORC_ERR_ARG;
+  if (block_table && (max_pages < 1 || num_pages < 1 || cap != max_pages * ORC_PAGE))
+    return ORC_ERR_ARG;
+  if (!rows) n_rows = B * ORC_HEADS;
+  if (n_rows < 0) return ORC_ERR_ARG;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+
+  orc_job j;
+  memset(&j, 0, sizeof j);
+  j.dtype = dtype; j.q = q; j.k = k; j.v = v;
+  j.seq_lens = seq_lens; j.block_table = block_table;
+  j.B = B; j.cap = cap; j.max_pages = max_pages; j.num_pages = num_pages;
+  j.KV = KV; j.D = D; j.window = window;
+  j.rows = rows; j.n_rows = n_rows; j.out = out;
+  pthread_mutex_init(&j.mu, NULL);
+
+  pthread_t th[256];
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t)
+    if (pthread_create(&th[started], NULL, orc_worker, &j) == 0) ++started;
+  orc_worker(&j);
+  for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+  pthread_mutex_destroy(&j.mu);
+  return j.err;
+}
