@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X decode-attention library.
+
+One step is one pass of the whole decode-attention hot path over one batch of
+synthetic input: a slidingDecodeGQA call on the contiguous bf16 cache of
+B=256 sequences (S_max 8192, seq_lens uniform in [1, 8192], window 1024) and a
+decodeGQA call on the paged bf16 cache of B=32 sequences (seq_lens uniform in
+[16384, 131072], page 16, random page permutation) -- the split kernels, the
+split-S combine and the paged addressing all run every step.  Inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line: value = algorithmic K/V bytes of the step / step time
+(GB/s), with per-kernel launch durations taken from HIP events the library
+records on its launch stream during the timed region, the roofline of the
+dominant kernel against the 8 TB/s HBM3E peak, and the fp64 CPU oracle timed on
+a bounded sample of the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = ("decode-attn K/V read GB/s and % of HBM peak; µs per call "
+          "(sliding B=256, global B=32)")
+SLIDING = "sliding_bf16_b256_s8192"
+GLOBAL = "global_bf16_b32_paged_s16k_128k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd", "csrc",
+                             "gqa_decode.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a profiler)")
+    ap.add_argument("--cpu-sample-seqs", type=str, default="64,8",
+                    help="sequences of the sliding,global workloads the oracle is timed on")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 --pmc
+    runs, valid only if taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = v
+    if vals.get("source_sha256") != source_hash():
+        return None
+    try:
+        return float(vals["global_split_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def oracle_sample(sl_case, gl_case, n_sl, n_gl, threads):
+    """Time the fp64 oracle on whole sequences of both workloads (all 32 heads)."""
+    import torch
+    import oracle
+    import synth
+
+    def sub_contig(c, bs):
+        out = []
+        for b in bs:
+            out.append(synth.Case(c.variant, c.dtype, c.q[b:b + 1].cpu(), c.k[b:b + 1].cpu(),
+                                  c.v[b:b + 1].cpu(), c.seq_lens[b:b + 1].cpu(), None, c.cap,
+                                  c.window))
+        return out
+
+    def sub_paged(c, bs):
+        out = []
+        bt = c.block_table.cpu()
+        for b in bs:
+            L = int(c.seq_lens[b])
+            npg = (L + 15) // 16
+            phys = bt[b, :npg].to(c.k.device, torch.int64)
+            kb, vb = c.k[phys].cpu(), c.v[phys].cpu()
+            tb = torch.full((1, bt.shape[1]), -1, dtype=torch.int32)
+            tb[0, :npg] = torch.arange(npg, dtype=torch.int32)
+            out.append(synth.Case(c.variant, c.dtype, c.q[b:b + 1].cpu(), kb, vb,
+                                  c.seq_lens[b:b + 1].cpu(), tb, c.cap, c.window))
+        return out
+
+    cases = sub_contig(sl_case, range(n_sl)) + sub_paged(gl_case, range(n_gl))
+    nbytes = sum(c.kv_bytes() for c in cases)
+    t0 = time.perf_counter()
+    for c in cases:
+        bt = None if c.block_table is None else synth.to_numpy(c.block_table)
+        oracle.gqa_decode(c.variant, synth.to_numpy(c.q), synth.to_numpy(c.k),
+                          synth.to_numpy(c.v), synth.to_numpy(c.seq_lens), block_table=bt,
+                          nthreads=threads)
+    dt = time.perf_counter() - t0
+    return nbytes, dt
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this decode-attention library runs on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_slidingdecodegqa_amd as gqa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gqa.library()
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    log("generating the sliding B=256 contiguous cache")
+    sl = synth.make_workload(SLIDING, seed=args.seed, device=dev, fill=0.0)
+    log("generating the global B=32 paged cache")
+    gl = synth.make_workload(GLOBAL, seed=args.seed, device=dev, fill=0.0)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
+    sl_bytes, gl_bytes = sl.kv_bytes(), gl.kv_bytes()
+
+    o_sl = torch.empty_like(sl.q)
+    o_gl = torch.empty_like(gl.q)
+    ws_sl_n = gqa.gqa_decode_workspace_bytes("sliding", sl.B, sl.cap)
+    ws_gl_n = gqa.gqa_decode_workspace_bytes("global", gl.B, gl.cap)
+    ws_sl = torch.empty(max(ws_sl_n, 256), dtype=torch.uint8, device=dev)
+    ws_gl = torch.empty(max(ws_gl_n, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gqa.gqa_decode_sliding(sl.q, sl.k, sl.v, sl.seq_lens, o=o_sl, workspace=ws_sl,
+                               stream=stream)
+        gqa.gqa_decode_global_paged(gl.q, gl.k, gl.v, gl.block_table, gl.seq_lens, o=o_gl,
+                                    workspace=ws_gl, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    gqa.profile_begin(4 * args.steps + 8)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    prof = gqa.profile_read()
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    def avg(key):
+        n, t = prof[key]
+        return t / n if n else 0.0
+
+    sl_ms = avg(("sliding", "split")) + avg(("sliding", "combine"))
+    gl_split_ms = avg(("global", "split"))
+    gl_comb_ms = avg(("global", "combine"))
+    gl_ms = gl_split_ms + gl_comb_ms
+    total_bytes = sl_bytes + gl_bytes
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+    achieved = gl_bytes / (gl_split_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    n_split_gl, tps_gl = gqa.gqa_decode_plan("global", gl.B, gl.cap)
+    n_split_sl, tps_sl = gqa.gqa_decode_plan("sliding", sl.B, sl.cap)
+    config = {
+        "workload": f"{SLIDING} + {GLOBAL}",
+        "sliding": {
+            "B": sl.B, "S_max": sl.cap, "kv_heads": 16, "head_dim": 256, "window": 1024,
+            "cache": "contiguous", "kv_bytes_per_call": sl_bytes,
+            "us_per_call": round(sl_ms * 1e3, 2),
+            "kv_GBps": round(sl_bytes / (sl_ms * 1e-3) / 1e9, 1) if sl_ms else None,
+            "frac_of_hbm_peak": round(sl_bytes / (sl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if sl_ms else None,
+            "n_split": n_split_sl, "tiles_per_split": tps_sl,
+        },
+        "global": {
+            "B": gl.B, "max_pages": gl.block_table.shape[1], "num_pages": gl.k.shape[0],
+            "kv_heads": 4, "head_dim": 512, "cache": "paged16", "kv_bytes_per_call": gl_bytes,
+            "us_per_call": round(gl_ms * 1e3, 2),
+            "split_kernel_us": round(gl_split_ms * 1e3, 2),
+            "combine_kernel_us": round(gl_comb_ms * 1e3, 2),
+            "kv_GBps": round(gl_bytes / (gl_ms * 1e-3) / 1e9, 1) if gl_ms else None,
+            "frac_of_hbm_peak": round(gl_bytes / (gl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if gl_ms else None,
+            "n_split": n_split_gl, "tiles_per_split": tps_gl,
+        },
+    }
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; unit-RMS values, RMS-normed weighted q/k)",
+        "config": config,
+        "roofline": {
+            "kernel": "gqa_split_kernel<4,512,paged,bf16> (decodeGQA, B=32 paged)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        n_sl, n_gl = (int(x) for x in args.cpu_sample_seqs.split(","))
+        threads = min(os.cpu_count() or 1, 16)
+        log(f"timing the fp64 oracle on {n_sl} sliding + {n_gl} global sequences, "
+            f"{threads} threads")
+        nb, dt = oracle_sample(sl, gl, n_sl, n_gl, threads)
+        line["cpu_baseline"] = {
+            "value": round(nb / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": (f"fp64 C oracle, all 32 heads of the first {n_sl} sequences of the "
+                       f"sliding B=256 cache and the first {n_gl} of the global B=32 paged "
+                       f"cache: {nb / 1e9:.3f} GB of K/V in {dt:.2f} s"),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

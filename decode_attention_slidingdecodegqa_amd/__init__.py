@@ -1,0 +1,39 @@
+"""MI355X (gfx950) decode attention for the Gemma-4-31B text decoder.
+
+Thin Python binding over the C ABI of ``libgqadecode.so`` (declared in
+``include/gqa_decode.h``).  The functions carry the C names and only marshal
+arguments: torch tensors provide device memory and the current stream, every
+step of the computation runs in the HIP kernels.  There is no fallback: when
+the library is missing or no GPU is present the calls raise.
+
+    gqa_decode_sliding(q, k, v, seq_lens)               slidingDecodeGQA, contiguous cache
+    gqa_decode_global(q, k, v, seq_lens)                decodeGQA, contiguous cache
+    gqa_decode_sliding_paged(q, k_pool, v_pool, block_table, seq_lens)
+    gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens)
+
+Shapes (attn.core of the gemma-4-31B Model Spec page): q [B,32,D]; contiguous
+k/v [B,S_max,KV,D]; paged pools [num_pages,16,KV,D] with block_table
+[B,max_pages] int32; seq_lens [B] int32; returns o [B,32,D] of q's dtype
+(float32 or bfloat16).  Sliding: KV=16, D=256, window 1024.  Global: KV=4, D=512.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    GQA_BF16,
+    GQA_F32,
+    GQA_GLOBAL,
+    GQA_SLIDING,
+    GqaError,
+    constants,
+    gqa_decode_global,
+    gqa_decode_global_paged,
+    gqa_decode_plan,
+    gqa_decode_sliding,
+    gqa_decode_sliding_paged,
+    gqa_decode_workspace_bytes,
+    gqa_status_str,
+    library,
+    profile_begin,
+    profile_read,
+    EXPORTED_SYMBOLS,
+)

@@ -1,0 +1,143 @@
+/*
+ * gqa_decode.h -- C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * The operation is the attn.core node of the gemma-4-31B Model Spec page
+ * (docs.theformalera.com/models/gemma-4-31b.md), "Compute-graph nodes" table:
+ *
+ *   slidingDecodeGQA  o[b,h] = sum_s softmax_s(1 * <q[b,h], k[b,s,h/2]>) * v[b,s,h/2]
+ *                     over the last 1024 positions s < seq_lens[b]
+ *                     (32 query heads, 16 kv heads, D = 256, scale 1, window 1024)
+ *   decodeGQA         the same with kv head h/8 over every s < seq_lens[b]
+ *                     (32 query heads, 4 kv heads, D = 512, scale 1)
+ *
+ * Argument order and shapes follow the page's "Tensors of the main nodes"
+ * table (q [B,32,D], k [B,S,kv,D], v [B,S,kv,D], seq_lens [B], o [B,32,D]); the
+ * paged forms use the page size 16 of the "At a glance" table (Shape domain
+ * row), which also bounds B to [1,256] and S to [1,262144].
+ *
+ * Window reading: the newest token is already in the cache when attention
+ * runs (the compact forward pass on the "Gemma 4 31B-it Text Architecture"
+ * page appends K/V first and masks keys t-1024 < s <= t), so sequence b
+ * attends to positions [max(0, L-1024), L) with L = seq_lens[b].
+ *
+ * Layouts (all row-major, D innermost, element type `dtype` for q/k/v/o):
+ *   q            [B, 32, D]
+ *   contiguous   k, v [B, S_max, KV, D]: row (b, s, g) at ((b*S_max + s)*KV + g)*D
+ *   paged        k_pool, v_pool [num_pages, 16, KV, D]; logical position s of
+ *                sequence b is physical page block_table[b*max_pages + s/16],
+ *                slot s%16
+ *   block_table  [B, max_pages] int32
+ *   seq_lens     [B] int32
+ *   o            [B, 32, D]
+ *   workspace    fp32 scratch for split-S partial results, at least
+ *                gqa_decode_workspace_bytes(...) bytes (may be NULL when that is 0)
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library
+ * allocates no device memory, keeps no pointer after return and does not
+ * synchronise: work is queued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the buffers must stay valid until it completes.  Calls that
+ * share one workspace must be ordered on one stream.
+ *
+ * Host-checked preconditions (a negative status is returned and nothing is
+ * launched): non-null pointers; 1 <= B <= 256; 1 <= S_max <= 262144 or
+ * 1 <= max_pages*16 <= 262144 with num_pages >= 1; a known dtype; 16-byte
+ * aligned q, k, v, o and workspace; a large enough workspace.
+ *
+ * Device-resident preconditions (documented, not checked on the host, which
+ * would need a synchronisation): 1 <= seq_lens[b] <= capacity, and
+ * block_table[b][p] in [0, num_pages) for every page p holding an attended
+ * position.  Device behaviour outside them is memory-safe: seq_lens is
+ * clamped to the capacity, seq_lens <= 0 gives a zero output row, a page id
+ * outside [0, num_pages) is never dereferenced (its positions are dropped),
+ * and no K/V byte outside the attended range, and no block-table entry of a
+ * page without an attended position, is ever read.
+ *
+ * Errors: HIP launch failures map to GQA_ERR_HIP.  The library never aborts
+ * and never prints.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v and o */
+enum { GQA_F32 = 0, GQA_BF16 = 1 };
+
+/* variant selector for the query functions */
+enum { GQA_SLIDING = 0, GQA_GLOBAL = 1 };
+
+/* status codes */
+enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL = -1,      /* a required pointer is NULL */
+  GQA_ERR_SHAPE = -2,     /* B, S_max, max_pages, num_pages or window out of range */
+  GQA_ERR_DTYPE = -3,     /* unknown dtype or variant */
+  GQA_ERR_ALIGN = -4,     /* a tensor base pointer is not 16-byte aligned */
+  GQA_ERR_WORKSPACE = -5, /* workspace missing or smaller than required */
+  GQA_ERR_HIP = -6        /* the HIP runtime reported an error */
+};
+
+/* slidingDecodeGQA on a contiguous cache: k, v [B, S_max, 16, 256]. */
+int gqa_decode_sliding(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                       void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* decodeGQA on a contiguous cache: k, v [B, S_max, 4, 512]. */
+int gqa_decode_global(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                      void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* slidingDecodeGQA on a paged cache: k_pool, v_pool [num_pages, 16, 16, 256]. */
+int gqa_decode_sliding_paged(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* decodeGQA on a paged cache: k_pool, v_pool [num_pages, 16, 4, 512]. */
+int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
+                            int32_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
+ * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
+ * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:
+ * the workspace may then be NULL.  Returns 0 for out-of-range arguments too. */
+size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity);
+
+/* The split-S plan the library uses for these arguments: number of splits per
+ * (sequence, kv head) and 16-position tiles per split.  Returns GQA_OK or
+ * GQA_ERR_SHAPE / GQA_ERR_DTYPE. */
+int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* n_split,
+                    int32_t* tiles_per_split);
+
+/* Compile-time constants of a variant (heads, kv heads, head dim, window, page).
+ * window is 0 for decodeGQA.  Returns GQA_OK or GQA_ERR_DTYPE. */
+int gqa_decode_constants(int32_t variant, int32_t* heads, int32_t* kv_heads, int32_t* head_dim,
+                         int32_t* window, int32_t* page);
+
+/* Static description of a status code. */
+const char* gqa_status_str(int32_t status);
+
+/* Launch timing for measurement: while enabled, every kernel the library
+ * launches is bracketed by HIP events recorded on its stream (at most
+ * `capacity` launches are kept).  gqa_profile_read synchronises those events
+ * and reports, per kernel kind, the number of launches and their summed
+ * duration in milliseconds (kind 2*variant: split kernel of that variant,
+ * 2*variant+1: its combine kernel); it also disables recording and releases
+ * the events.  Measurement only: not thread-safe, not for captured graphs. */
+int gqa_profile_begin(int32_t capacity);
+int gqa_profile_read(int32_t* counts, double* total_ms, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

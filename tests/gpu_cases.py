@@ -1,0 +1,60 @@
+"""Helpers shared by the GPU parity tests: run a synth.Case through the HIP
+library (via the C-ABI binding) and through the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import decode_attention_slidingdecodegqa_amd as gqa
+import oracle
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}  # max-abs error bars for unit-RMS values
+
+
+def hip_run(case: synth.Case, workspace=None, stream=None, o=None) -> torch.Tensor:
+    if case.variant == "sliding":
+        fn_c, fn_p = gqa.gqa_decode_sliding, gqa.gqa_decode_sliding_paged
+    else:
+        fn_c, fn_p = gqa.gqa_decode_global, gqa.gqa_decode_global_paged
+    if case.block_table is None:
+        return fn_c(case.q, case.k, case.v, case.seq_lens, o=o, workspace=workspace,
+                    stream=stream)
+    return fn_p(case.q, case.k, case.v, case.block_table, case.seq_lens, o=o,
+                workspace=workspace, stream=stream)
+
+
+def oracle_run(case: synth.Case, rows=None, window=None, nthreads=16) -> np.ndarray:
+    bt = None if case.block_table is None else synth.to_numpy(case.block_table)
+    return oracle.gqa_decode((case.KV, case.D, case.window if window is None else window),
+                             synth.to_numpy(case.q), synth.to_numpy(case.k),
+                             synth.to_numpy(case.v), synth.to_numpy(case.seq_lens),
+                             block_table=bt, rows=rows, nthreads=nthreads)
+
+
+def to_f64(o: torch.Tensor) -> np.ndarray:
+    return o.detach().to(torch.float64).cpu().numpy()
+
+
+def max_err(a: np.ndarray, b: np.ndarray) -> float:
+    if a.size == 0:
+        return 0.0
+    d = np.abs(a - b)
+    if not np.isfinite(d).all():
+        return float("inf")
+    return float(d.max())
+
+
+def to_gpu(case: synth.Case) -> synth.Case:
+    dev = "cuda"
+    return synth.Case(case.variant, case.dtype, case.q.to(dev), case.k.to(dev), case.v.to(dev),
+                      case.seq_lens.to(dev),
+                      None if case.block_table is None else case.block_table.to(dev),
+                      case.cap, case.window)
+
+
+def to_cpu(case: synth.Case) -> synth.Case:
+    return synth.Case(case.variant, case.dtype, case.q.cpu(), case.k.cpu(), case.v.cpu(),
+                      case.seq_lens.cpu(),
+                      None if case.block_table is None else case.block_table.cpu(),
+                      case.cap, case.window)

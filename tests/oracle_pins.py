@@ -157,22 +157,31 @@ def one_hot_case(variant, dtype, B, cap, lens, positions, seed, paged=False):
     for h in range(HEADS):
         q[:, h, js[h]] = 1.0
     c.q = q.to(c.q.dtype)
-
-    def set_key(b, s, g, j, val):
-        if c.block_table is None:
-            c.k[b, s, g, j] = val
-        else:
-            c.k[int(c.block_table[b, s // 16]), s % 16, g, j] = val
-
     for b in range(B):
         lo, L = c.attended(b)
+        s = torch.arange(lo, L)
+        if c.block_table is None:
+            page, slot = None, None
+        else:
+            page = c.block_table[b, s // 16].long()
+            slot = s % 16
         for h in range(HEADS):
             g = h // G
-            for s in range(lo, L):
-                set_key(b, s, g, js[h], float(torch.empty(()).uniform_(-4, 4, generator=gen)))
+            vals = torch.empty(L - lo).uniform_(-4, 4, generator=gen)
+            vals[s == positions[b]] = 160.0
+            vals = vals.to(c.k.dtype)
+            if page is None:
+                c.k[b, lo:L, g, js[h]] = vals
+            else:
+                c.k[page, slot, g, js[h]] = vals
+    # the dominant key component of every head of the group at positions[b]
+    for b in range(B):
         p = positions[b]
         for h in range(HEADS):
-            set_key(b, p, h // G, js[h], 160.0)
+            if c.block_table is None:
+                c.k[b, p, h // G, js[h]] = 160.0
+            else:
+                c.k[int(c.block_table[b, p // 16]), p % 16, h // G, js[h]] = 160.0
     return c
 
 

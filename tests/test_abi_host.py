@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, plans sensibly and rejects bad arguments before launching anything.
+No call here reaches the GPU: every entry-point call below fails validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_slidingdecodegqa_amd as gqa
+from decode_attention_slidingdecodegqa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY_PATH):
+        from decode_attention_slidingdecodegqa_amd import build
+        build.build()
+    return gqa.library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(gqa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_constants_match_pages(lib):
+    gold = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "model_constants.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = (x.strip() for x in line.split("="))
+            gold[k] = int(v)
+    s = gqa.constants("sliding")
+    gl = gqa.constants("global")
+    assert s == dict(heads=gold["heads"], kv_heads=gold["sliding.kv_heads"],
+                     head_dim=gold["sliding.head_dim"], window=gold["sliding.window"],
+                     page=gold["page_size"])
+    assert gl == dict(heads=gold["heads"], kv_heads=gold["global.kv_heads"],
+                      head_dim=gold["global.head_dim"], window=0, page=gold["page_size"])
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+@pytest.mark.parametrize("B,cap", [(1, 1), (1, 262144), (4, 2048), (4, 4096), (32, 131072),
+                                   (256, 8192), (256, 262144), (7, 33)])
+def test_plan_covers_every_tile(lib, variant, B, cap):
+    n_split, tps = gqa.gqa_decode_plan(variant, B, cap)
+    KV = 16 if variant == "sliding" else 4
+    tiles = (cap + 15) // 16
+    if variant == "sliding":
+        tiles = min(tiles, 1024 // 16 + 1)
+    assert n_split >= 1 and tps >= 1
+    assert n_split * tps >= tiles                     # every attended tile has a split
+    assert (n_split - 1) * tps < tiles                # no split is empty for the longest unit
+    ws = gqa.gqa_decode_workspace_bytes(variant, B, cap)
+    if n_split == 1:
+        assert ws == 0
+    else:
+        G, D = 32 // KV, (256 if variant == "sliding" else 512)
+        assert ws >= B * KV * n_split * G * (D + 2) * 4
+
+
+def test_plan_examples(lib):
+    # many (sequence, kv head) units: one split, the work-group covers the window
+    assert gqa.gqa_decode_plan("sliding", 256, 8192)[0] == 1
+    # few units over long caches: split-S
+    n, t = gqa.gqa_decode_plan("global", 32, 131072)
+    assert n > 1 and t * 16 <= 2048
+    n, t = gqa.gqa_decode_plan("global", 1, 262144)
+    assert n * 4 >= 256                               # at least one work-group per CU
+
+
+def test_bad_arguments_fail_before_launch(lib):
+    P = ctypes.c_void_p
+    ok = P(0x10000)  # aligned non-null stand-ins; never dereferenced: validation fails first
+    mis = P(0x10008)
+    sl = lib.gqa_decode_sliding
+    gl = lib.gqa_decode_global_paged
+    E = {"NULL": -1, "SHAPE": -2, "DTYPE": -3, "ALIGN": -4, "WS": -5}
+    # null pointers
+    assert sl(None, ok, ok, ok, ok, 4, 2048, 1, None, 0, None) == E["NULL"]
+    assert sl(ok, ok, ok, None, ok, 4, 2048, 1, None, 0, None) == E["NULL"]
+    assert gl(ok, ok, ok, None, 10, ok, ok, 4, 10, 1, None, 0, None) == E["NULL"]
+    # batch and capacity ranges
+    assert sl(ok, ok, ok, ok, ok, 0, 2048, 1, None, 0, None) == E["SHAPE"]
+    assert sl(ok, ok, ok, ok, ok, 257, 2048, 1, None, 0, None) == E["SHAPE"]
+    assert sl(ok, ok, ok, ok, ok, 4, 0, 1, None, 0, None) == E["SHAPE"]
+    assert sl(ok, ok, ok, ok, ok, 4, 262145, 1, None, 0, None) == E["SHAPE"]
+    assert gl(ok, ok, ok, ok, 0, ok, ok, 4, 10, 1, None, 0, None) == E["SHAPE"]
+    assert gl(ok, ok, ok, ok, 16385, ok, ok, 4, 10, 1, None, 0, None) == E["SHAPE"]
+    assert gl(ok, ok, ok, ok, 10, ok, ok, 4, 0, 1, None, 0, None) == E["SHAPE"]
+    # dtype
+    assert sl(ok, ok, ok, ok, ok, 4, 2048, 2, None, 0, None) == E["DTYPE"]
+    assert sl(ok, ok, ok, ok, ok, 4, 2048, -1, None, 0, None) == E["DTYPE"]
+    # alignment
+    assert sl(mis, ok, ok, ok, ok, 256, 8192, 1, None, 0, None) == E["ALIGN"]
+    assert sl(ok, ok, mis, ok, ok, 256, 8192, 1, None, 0, None) == E["ALIGN"]
+    assert sl(ok, ok, ok, ok, mis, 256, 8192, 1, None, 0, None) == E["ALIGN"]
+    # workspace: B=32 global paged over 131072 positions needs one
+    need = lib.gqa_decode_workspace_bytes(1, 32, 131072)
+    assert need > 0
+    assert gl(ok, ok, ok, ok, 8192, ok, ok, 32, 9000, 1, None, 0, None) == E["WS"]
+    assert gl(ok, ok, ok, ok, 8192, ok, ok, 32, 9000, 1, ok, need - 1, None) == E["WS"]
+    assert gl(ok, ok, ok, ok, 8192, ok, ok, 32, 9000, 1, mis, need, None) == E["ALIGN"]
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert gqa.gqa_status_str(code)
+    assert gqa.gqa_status_str(-99) == "unknown status"
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    q = torch.zeros(1, 32, 256, dtype=torch.bfloat16)
+    k = torch.zeros(1, 16, 16, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gqa.gqa_decode_sliding(q, k, k, torch.ones(1, dtype=torch.int32))
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read().lower()
+                assert "oracle" not in src, f
+    assert "oracle" not in open(HEADER).read().lower()

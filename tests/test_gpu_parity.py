@@ -1,0 +1,250 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on an MI355X.
+
+Every case is seeded and synthetic (synth.py).  Tolerances: max-abs error 1e-4
+for float32 inputs, 2e-2 for bfloat16 inputs (unit-RMS values).  Invariants
+that the method makes exact are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_slidingdecodegqa_amd as gqa
+import oracle_pins
+import synth
+from gpu_cases import TOL, hip_run, max_err, oracle_run, to_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+HEADS = 32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but no GPU is visible")
+    gqa.library()
+
+
+SMALL = {
+    # variant: (cap, seq_lens) spanning several tiles, the window edge and ragged tails
+    "sliding": (2096, [1, 15, 16, 17, 1023, 1024, 1025, 1041, 2047, 2096]),
+    "global": (1312, [1, 15, 16, 17, 100, 513, 1024, 1299, 1312]),
+}
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_parity_small(variant, dtype, paged):
+    cap, lens = SMALL[variant]
+    c = synth.make_case(variant, dtype, len(lens), cap, lens, paged=paged, seed=101,
+                        extra_pages=5)
+    ref = oracle_run(c)
+    got = to_f64(hip_run(to_gpu(c)))
+    err = max_err(got, ref)
+    assert err <= TOL[dtype], (variant, dtype, paged, err)
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_parity_batch_shapes(variant):
+    # many sequences (direct path) and one sequence (split path) of one dtype
+    for B, cap, seed in ((64, 1100, 1), (1, 9000, 2), (3, 4096, 3)):
+        lens = synth.draw_seq_lens(("uniform", 1, cap), B, seed)
+        c = synth.make_case(variant, "bf16", B, cap, lens, seed=seed)
+        err = max_err(to_f64(hip_run(to_gpu(c))), oracle_run(c))
+        assert err <= TOL["bf16"], (B, cap, err)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_single_position_is_exact(variant, dtype, paged):
+    c = synth.make_case(variant, dtype, 3, 64, [1, 1, 1], paged=paged, seed=102)
+    got = hip_run(to_gpu(c)).cpu()
+    G = HEADS // c.KV
+    for b in range(3):
+        for h in range(HEADS):
+            exp = oracle_pins.value_row(c, b, 0, h // G)
+            assert torch.equal(got[b, h], exp), (b, h)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_one_hot_dominant_logit_selects_exactly(variant, dtype, paged):
+    lens = [1030, 200, 47, 1024, 1296]
+    cap = 1296
+    n_split, tps = gqa.gqa_decode_plan(variant, len(lens), cap)
+    for pick in ("lo", "last", "page0", "page15", "split"):
+        pos = []
+        for L in lens:
+            lo = max(0, L - 1024) if variant == "sliding" else 0
+            first = ((lo + 15) // 16) * 16
+            p = {"lo": lo, "last": L - 1, "page0": first, "page15": first + 15,
+                 "split": (lo // 16 + tps) * 16}[pick]
+            pos.append(min(p, L - 1))
+        c = oracle_pins.one_hot_case(variant, dtype, len(lens), cap, lens, pos, seed=103,
+                                     paged=paged)
+        got = hip_run(to_gpu(c)).cpu()
+        G = HEADS // c.KV
+        for b in range(len(lens)):
+            for h in range(HEADS):
+                exp = oracle_pins.value_row(c, b, pos[b], h // G)
+                assert torch.equal(got[b, h], exp), (pick, b, h)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_poison_outside_the_range_is_never_read(variant, paged):
+    lens = [1300, 20, 1025, 16, 2000]
+    kw = dict(paged=paged, seed=104, extra_pages=6)
+    a = synth.make_case(variant, "bf16", 5, 2000, lens, fill=float("nan"), **kw)
+    z = synth.make_case(variant, "bf16", 5, 2000, lens, fill=0.0, **kw)
+    ga = hip_run(to_gpu(a)).cpu()
+    gz = hip_run(to_gpu(z)).cpu()
+    assert torch.isfinite(ga.float()).all()
+    assert torch.equal(ga, gz)
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_paged_equals_contiguous_bitwise(variant):
+    lens = [1, 95, 1040, 700]
+    c = synth.make_case(variant, "bf16", 4, 1040, lens, seed=105)
+    p = oracle_pins._contig_to_paged(c, seed=106)
+    a = hip_run(to_gpu(c)).cpu()
+    b = hip_run(to_gpu(p)).cpu()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_gqa_group_sharing_bitwise(variant):
+    c = synth.make_case(variant, "bf16", 2, 700, [700, 333], seed=107)
+    G = HEADS // c.KV
+    for h in range(HEADS):
+        c.q[:, h] = c.q[:, (h // G) * G]
+    got = hip_run(to_gpu(c)).cpu()
+    for h in range(HEADS):
+        assert torch.equal(got[:, h], got[:, (h // G) * G])
+
+
+def test_sliding_equals_full_below_the_window():
+    c = synth.make_case("sliding", "f32", 4, 1024, [1, 513, 1000, 1024], seed=108)
+    got = to_f64(hip_run(to_gpu(c)))
+    full = oracle_run(c, window=0)
+    assert max_err(got, full) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_length_edge_cases(variant):
+    # seq_len 0 and negative give zero rows; above the capacity clamps to it
+    cap = 320
+    c = synth.make_case(variant, "bf16", 4, cap, [0, -5, cap, 17], seed=109, fill=0.0)
+    got = hip_run(to_gpu(c)).cpu()
+    assert torch.count_nonzero(got[0]) == 0 and torch.count_nonzero(got[1]) == 0
+    c2 = synth.Case(c.variant, c.dtype, c.q, c.k, c.v,
+                    torch.tensor([0, -5, cap + 1000, 17], dtype=torch.int32), None, cap, c.window)
+    got2 = hip_run(to_gpu(c2)).cpu()
+    assert torch.equal(got, got2)
+    ref = oracle_run(c)
+    assert max_err(to_f64(got), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_deterministic_and_workspace_reuse(variant):
+    cap = 4096
+    lens_a = [4096, 5, 3000, 1]
+    lens_b = [17, 4000, 64, 2222]
+    a = to_gpu(synth.make_case(variant, "bf16", 4, cap, lens_a, seed=110))
+    b = to_gpu(synth.make_case(variant, "bf16", 4, cap, lens_b, seed=111))
+    need = gqa.gqa_decode_workspace_bytes(variant, 4, cap)
+    ws = torch.full((max(need, 16),), 255, dtype=torch.uint8, device="cuda")  # NaN-patterned
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1 = hip_run(a, workspace=ws, stream=s)
+        ob = hip_run(b, workspace=ws, stream=s)
+        o2 = hip_run(a, workspace=ws, stream=s)
+    s.synchronize()
+    assert torch.equal(o1, o2)
+    assert max_err(to_f64(ob), oracle_run(b)) <= TOL["bf16"]
+
+
+def test_profile_hooks_count_launches():
+    c = to_gpu(synth.make_case("global", "bf16", 2, 4096, [4096, 100], seed=112))
+    gqa.profile_begin(16)
+    for _ in range(3):
+        hip_run(c)
+    res = gqa.profile_read()
+    n_split, _ = gqa.gqa_decode_plan("global", 2, 4096)
+    assert res[("global", "split")][0] == 3 and res[("global", "split")][1] > 0
+    assert res[("global", "combine")][0] == (3 if n_split > 1 else 0)
+    assert res[("sliding", "split")][0] == 0
+
+
+# --------------------------------------------------------------- full-size workloads
+
+def _sample_rows(case, n_seq, seed):
+    g = torch.Generator().manual_seed(seed)
+    bs = torch.randperm(case.B, generator=g)[:n_seq].tolist()
+    return [(b, h) for b in bs for h in range(HEADS)]
+
+
+@pytest.mark.parametrize("name", ["sliding_f32_b4_s2048", "global_bf16_b4_s4096"])
+def test_workload_small_full_parity(name):
+    c = synth.make_workload(name, seed=0)
+    got = to_f64(hip_run(to_gpu(c)))
+    err = max_err(got, oracle_run(c))
+    assert err <= TOL[c.dtype], (name, err)
+
+
+def test_workload_sliding_b256_sampled():
+    name = "sliding_bf16_b256_s8192"
+    c = synth.make_workload(name, seed=0, device="cuda")
+    got = hip_run(c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got.float()).all()
+    lens = c.seq_lens.cpu()
+    # sampled sequences, incl. the shortest and the longest: the oracle on their slice
+    order = torch.argsort(lens)
+    pick = sorted(set([int(order[0]), int(order[-1])] +
+                      torch.randperm(c.B, generator=torch.Generator().manual_seed(5))[:6].tolist()))
+    for b in pick:
+        sub = synth.Case(c.variant, c.dtype, c.q[b:b + 1].cpu(), c.k[b:b + 1].cpu(),
+                         c.v[b:b + 1].cpu(), lens[b:b + 1], None, c.cap, c.window)
+        err = max_err(to_f64(got[b:b + 1]), oracle_run(sub))
+        assert err <= TOL["bf16"], (b, int(lens[b]), err)
+
+
+def test_workload_global_b32_paged_sampled():
+    name = "global_bf16_b32_paged_s16k_128k"
+    c = synth.make_workload(name, seed=0, device="cuda")
+    got = hip_run(c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got.float()).all()
+    host = synth.Case(c.variant, c.dtype, c.q.cpu(), c.k.cpu(), c.v.cpu(), c.seq_lens.cpu(),
+                      c.block_table.cpu(), c.cap, c.window)
+    lens = host.seq_lens
+    order = torch.argsort(lens)
+    bs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    rows = [(b, h) for b in bs for h in (0, 7, 8, 31)]
+    ref = oracle_run(host, rows=rows)
+    gh = to_f64(got)
+    for i, (b, h) in enumerate(rows):
+        err = max_err(gh[b, h], ref[i])
+        assert err <= TOL["bf16"], (b, h, int(lens[b]), err)
+
+
+@pytest.mark.parametrize("name", ["sliding_bf16_b1_paged_s262144",
+                                  "global_bf16_b1_paged_s262144"])
+def test_workload_long_single_sequence(name):
+    c = synth.make_workload(name, seed=0, device="cuda")
+    got = hip_run(c)
+    torch.cuda.synchronize()
+    host = synth.Case(c.variant, c.dtype, c.q.cpu(), c.k.cpu(), c.v.cpu(), c.seq_lens.cpu(),
+                      c.block_table.cpu(), c.cap, c.window)
+    heads = range(HEADS) if c.variant == "sliding" else (0, 9, 22, 31)
+    rows = [(0, h) for h in heads]
+    ref = oracle_run(host, rows=rows)
+    gh = to_f64(got)
+    for i, (b, h) in enumerate(rows):
+        err = max_err(gh[b, h], ref[i])
+        assert err <= TOL["bf16"], (h, err)
