@@ -51,7 +51,35 @@ def parse():
                     help="skip the oracle timing (e.g. under a profiler)")
     ap.add_argument("--cpu-sample-seqs", type=str, default="64,8",
                     help="sequences of the sliding,global workloads the oracle is timed on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (calibrates the HBM "
+                         "byte counters of a profiler) and exit")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int) -> None:
+    """Plain device kernels of known size on random data: an elementwise copy
+    (reads nbytes, writes nbytes) and a sum (reads nbytes)."""
+    import torch
+    n = nbytes // 4
+    g = torch.Generator(device="cuda").manual_seed(1)
+    src = torch.rand(n, dtype=torch.float32, device="cuda", generator=g)
+    dst = torch.empty_like(src)
+    out = {"copy_probe_bytes": n * 4}
+    for name, fn, moved in (("copy", lambda: torch.mul(src, 1.0, out=dst), 2 * n * 4),
+                            ("sum", lambda: src.sum(), n * 4)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 3
+        out[f"{name}_ms"] = round(ms, 4)
+        out[f"{name}_GBps"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(out), flush=True)
 
 
 def source_hash() -> str:
@@ -125,6 +153,10 @@ def main():
         print(f"bench.py: this decode-attention library runs on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     import decode_attention_slidingdecodegqa_amd as gqa

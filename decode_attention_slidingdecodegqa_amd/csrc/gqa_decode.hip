@@ -52,6 +52,9 @@ constexpr int kMaxBatch = 256;
 constexpr int kMaxSeq = 262144;
 constexpr int kSlidingWindow = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
+// raise the softmax reference max only when a tile exceeds it by more than
+// this (natural-log units): weights stay below e^8
+constexpr float kRescaleGap = 8.0f;
 
 // split planner: aim at ~8 work-groups per CU of a 256-CU part, with splits of
 // 4..128 tiles (64..2048 positions)
@@ -155,8 +158,16 @@ __device__ inline void store_run(char* dst, const float* v, int n) {
   }
 }
 
+// Waves per SIMD the split kernel is compiled for: the sliding bf16 kernel fits
+// two (<= 256 registers), the others need one.
+template <int KV, bool BF16>
+constexpr int split_waves_per_simd() {
+  return (KV == 16 && BF16) ? 2 : 1;
+}
+
 template <int KV, int D, bool PAGED, bool BF16>
-__global__ __launch_bounds__(kThreads) void gqa_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void gqa_split_kernel(
+    SplitArgs a) {
   constexpr int G = kHeads / KV;  // query heads per kv head
   constexpr int E = Elem<BF16>::E;
   constexpr int EB = Elem<BF16>::bytes;
@@ -205,65 +216,92 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(SplitArgs a) {
   // query heads of the group as the B operand of QK^T (columns >= G are zero)
   u32x4 qreg[KCH];
   {
-    const char* qrow = a.q + ((size_t)b * kHeads + g * G + r) * ROW;
+    const char* qrow = a.q + ((size_t)b * kHeads + g * G + (r < G ? r : 0)) * ROW;
 #pragma unroll
     for (int t = 0; t < KCH; ++t) {
-      qreg[t] = u32x4{0u, 0u, 0u, 0u};
-      if (r < G) qreg[t] = load16(qrow + (4 * t + j) * 16);
+      const u32x4 x = load16(qrow + (4 * t + j) * 16);
+      qreg[t] = r < G ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
+
+  // this wave takes tiles wg_t0 + wave + 4*i, i < n_mine; lane i holds the
+  // physical page of its i-th tile (one vector load instead of one dependent
+  // scalar load per tile)
+  const int first = wg_t0 + wave;
+  const int n_mine = first < wg_t1 ? (wg_t1 - first + kWaves - 1) / kWaves : 0;
+  int pages = 0;
+  if constexpr (PAGED) {
+    if (lane < n_mine) pages = a.block_table[(size_t)b * a.max_pages + first + kWaves * lane];
+  }
+
+  // Per-tile addressing.  Rows outside [lo, L) are clamped onto the nearest
+  // attended row of the same tile: every load is unconditional yet never
+  // leaves the attended range; the clamped duplicates are dropped below by
+  // setting their logits to -inf (so their softmax weight is exactly 0).
+  struct TileAt {
+    const char* kb;
+    const char* vb;
+    int pos0;
+    bool ok;  // page id inside the pool
+  };
+  auto tile_at = [&](int i) {
+    TileAt t;
+    const int tile = first + kWaves * i;
+    t.pos0 = tile * kTile;
+    size_t off;
+    if constexpr (PAGED) {
+      const int page = __builtin_amdgcn_readlane(pages, i);
+      t.ok = page >= 0 && page < a.num_pages;
+      off = ((size_t)(t.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+    } else {
+      t.ok = true;
+      off = (((size_t)b * a.cap + t.pos0) * KV + g) * (size_t)ROW;
+    }
+    t.kb = a.k + off;
+    t.vb = a.v + off;
+    return t;
+  };
+  auto clamp_row = [&](int pos0, int row) {
+    const int p = min(max(pos0 + row, rg.lo), rg.L - 1);
+    return p - pos0;
+  };
+
+  u32x4 kreg[KCH];       // key row r of the tile, chunks 4t+j
+  u32x4 vreg[4][VBLK];   // value rows 4j+i of the tile, chunks r+16*blk
+  auto load_k = [&](const TileAt& t) {
+    const char* row = t.kb + (size_t)clamp_row(t.pos0, r) * POS;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) kreg[c] = load16(row + (4 * c + j) * 16);
+  };
+  auto load_v = [&](const TileAt& t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* row = t.vb + (size_t)clamp_row(t.pos0, 4 * j + i) * POS;
+#pragma unroll
+      for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16(row + (r + 16 * blk) * 16);
+    }
+  };
 
   f32x4 acc[VBLK][E];
 #pragma unroll
   for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max of head r (equal on the 4 lanes of a column)
-  float l = 0.f;        // this lane's share of the running sum
+  // Reference max of head r (equal on the 4 lanes of a column).  It is raised
+  // only when a tile's max exceeds it by more than kRescaleGap, so weights
+  // stay below e^kRescaleGap and the O/l rescale runs a few times per wave
+  // instead of every tile; the result is the same softmax either way.
+  float m = -INFINITY;
+  float l = 0.f;  // this lane's share of the sum of weights
 
-  for (int tile = wg_t0 + wave; tile < wg_t1; tile += kWaves) {
-    const int pos0 = tile * kTile;
-    const char* kbase;
-    const char* vbase;
-    bool page_ok = true;
-    if constexpr (PAGED) {
-      const int page = a.block_table[(size_t)b * a.max_pages + tile];
-      page_ok = page >= 0 && page < a.num_pages;
-      const size_t off = ((size_t)(page_ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
-      kbase = a.k + off;
-      vbase = a.v + off;
-    } else {
-      const size_t off = (((size_t)b * a.cap + pos0) * KV + g) * (size_t)ROW;
-      kbase = a.k + off;
-      vbase = a.v + off;
-    }
-
-    // key row r of the tile: chunks 4t+j
-    u32x4 kreg[KCH];
-    {
-      const int p = pos0 + r;
-      const bool ok = page_ok && p >= rg.lo && p < rg.L;
-      const char* row = kbase + (size_t)r * POS;
-#pragma unroll
-      for (int t = 0; t < KCH; ++t) {
-        kreg[t] = u32x4{0u, 0u, 0u, 0u};
-        if (ok) kreg[t] = load16(row + (4 * t + j) * 16);
-      }
-    }
-    // value rows 4j+i of the tile: chunks r+16*blk
-    u32x4 vreg[4][VBLK];
-    bool vok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = pos0 + 4 * j + i;
-      vok[i] = page_ok && p >= rg.lo && p < rg.L;
-      const char* row = vbase + (size_t)(4 * j + i) * POS;
-#pragma unroll
-      for (int blk = 0; blk < VBLK; ++blk) {
-        vreg[i][blk] = u32x4{0u, 0u, 0u, 0u};
-        if (vok[i]) vreg[i][blk] = load16(row + (r + 16 * blk) * 16);
-      }
-    }
+  TileAt cur = tile_at(0);
+  if (n_mine > 0) {
+    load_k(cur);
+    load_v(cur);
+  }
+  for (int it = 0; it < n_mine; ++it) {
+    const bool more = it + 1 < n_mine;
+    const TileAt nxt = more ? tile_at(it + 1) : cur;
 
     // logits z[pos 4j+i][head r]
     f32x4 z;
@@ -292,36 +330,44 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(SplitArgs a) {
       }
       z = z0 + z1;
     }
+    // the key registers are free: fetch the next tile's keys
+    if (more) load_k(nxt);
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (!vok[i]) z[i] = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int p = cur.pos0 + 4 * j + i;
+      if (!(cur.ok && p >= rg.lo && p < rg.L)) z[i] = -INFINITY;
+    }
 
     // online softmax (fp32)
     float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_fast((m - m_use) * kLog2e);
+    const bool grow = tmax > m + kRescaleGap;  // also when m = -inf and tmax is finite
+    if (__any(grow)) {
+      const float m_next = grow ? tmax : m;
+      const float alpha = exp2_fast((m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+      if (grow) {
+        l *= alpha;
+#pragma unroll
+        for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[blk][e] *= alpha;
+      }
+      m = m_next;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
-    m = m_new;
-
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int blk = 0; blk < VBLK; ++blk)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[blk][e] *= alpha;
-    }
 
     if constexpr (BF16) {
       unsigned pb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = bf16_bits(p[i]);
-      l = l * alpha + ((bf16_value(pb[0]) + bf16_value(pb[1])) +
-                       (bf16_value(pb[2]) + bf16_value(pb[3])));
-      const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)});
+      l += (bf16_value(pb[0]) + bf16_value(pb[1])) + (bf16_value(pb[2]) + bf16_value(pb[3]));
+      const s16x4 pt =
+          __builtin_bit_cast(s16x4, u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)});
 #pragma unroll
       for (int blk = 0; blk < VBLK; ++blk) {
 #pragma unroll
@@ -335,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(SplitArgs a) {
         }
       }
     } else {
-      l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -345,6 +391,9 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(SplitArgs a) {
             acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e), p[i],
                                                                acc[blk][e], 0, 0, 0);
     }
+    // the value registers are free: fetch the next tile's values
+    if (more) load_v(nxt);
+    cur = nxt;
   }
 
   l += __shfl_xor(l, 16);
