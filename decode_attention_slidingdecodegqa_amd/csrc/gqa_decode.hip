@@ -124,6 +124,15 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Values are read exactly once, 256 contiguous bytes per row and instruction:
+// non-temporal loads keep them out of the caches and raise the sustained read
+// rate.  Keys are read in 64-byte halves of a 128-byte line by two consecutive
+// instructions; they use ordinary loads so the line is still cached for the
+// second half (non-temporal key loads measured slower).
+__device__ inline u32x4 load16_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ inline unsigned bf16_bits(float x) {
   return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
     for (int i = 0; i < 4; ++i) {
       const char* row = t.vb + (size_t)clamp_row(t.pos0, 4 * j + i) * POS;
 #pragma unroll
-      for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16(row + (r + 16 * blk) * 16);
+      for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16_stream(row + (r + 16 * blk) * 16);
     }
   };
 
@@ -481,10 +490,13 @@ struct CombineArgs {
 };
 
 // One work-group per (sequence, query head); thread t owns d = 4t .. 4t+3.
+// Splits whose l is 0 hold no result (their workspace slots may be stale):
+// their weight is 0 and their values are selected away, never multiplied.
 template <int KV, int D, bool BF16>
 __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   constexpr int G = kHeads / KV;
   constexpr int EB = Elem<BF16>::bytes;
+  constexpr int U = 8;  // partials in flight per thread
   const int b = blockIdx.x / kHeads;
   const int h = blockIdx.x % kHeads;
   const int g = h / G;
@@ -494,32 +506,41 @@ __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   int n_used = rg.t1 > rg.t0 ? (rg.t1 - rg.t0 + a.tps - 1) / a.tps : 0;
   n_used = n_used < a.n_split ? n_used : a.n_split;
 
-  const float* ml = a.ws_ml + (size_t)unit * a.n_split * G * 2;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + (size_t)unit * a.n_split * G + hh;
   float M = -INFINITY;
   for (int s = 0; s < n_used; ++s) {
-    const float ls = ml[(s * G + hh) * 2 + 1];
-    if (ls > 0.f) M = fmaxf(M, ml[(s * G + hh) * 2]);
+    const f32x2 x = ml[(size_t)s * G];
+    if (x[1] > 0.f) M = fmaxf(M, x[0]);
   }
   const int d = threadIdx.x * 4;
+  const float* accp = a.ws_acc + ((size_t)unit * a.n_split * G + hh) * D + d;
+  const size_t sstride = (size_t)G * D;
   f32x4 A = {0.f, 0.f, 0.f, 0.f};
   float Lt = 0.f;
-  for (int s = 0; s < n_used; ++s) {
-    const float ls = ml[(s * G + hh) * 2 + 1];
-    if (ls > 0.f) {
-      const float sc = exp2_fast((ml[(s * G + hh) * 2] - M) * kLog2e);
-      Lt += sc * ls;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(
-          a.ws_acc + (((size_t)unit * a.n_split + s) * G + hh) * D + d);
-      A += sc * x;
+  for (int s0 = 0; s0 < n_used; s0 += U) {
+    f32x4 x[U];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u < n_used ? s0 + u : n_used - 1;
+      const f32x2 e = ml[(size_t)s * G];
+      const bool ok = s0 + u < n_used && e[1] > 0.f;
+      w[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
+      Lt += w[u] * (ok ? e[1] : 0.f);
+      x[u] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride);
+      x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) A += w[u] * x[u];
   }
   float run[4];
   const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   for (int c = 0; c < 4; ++c) run[c] = Lt > 0.f ? A[c] * inv : 0.f;
   char* dst = a.o + ((size_t)b * kHeads + h) * D * EB + (size_t)d * EB;
   if constexpr (BF16) {
-    *reinterpret_cast<u32x2*>(dst) =
-        u32x2{bf16_bits(run[0]) | (bf16_bits(run[1]) << 16), bf16_bits(run[2]) | (bf16_bits(run[3]) << 16)};
+    *reinterpret_cast<u32x2*>(dst) = u32x2{bf16_bits(run[0]) | (bf16_bits(run[1]) << 16),
+                                           bf16_bits(run[2]) | (bf16_bits(run[3]) << 16)};
   } else {
     *reinterpret_cast<f32x4*>(dst) = f32x4{run[0], run[1], run[2], run[3]};
   }
