@@ -32,6 +32,8 @@ from ._lib import (  # noqa: F401
     gqa_decode_sliding_paged,
     gqa_decode_workspace_bytes,
     gqa_status_str,
+    hbm_copy_probe,
+    hbm_read_probe,
     library,
     profile_begin,
     profile_read,

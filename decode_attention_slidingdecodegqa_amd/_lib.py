@@ -18,6 +18,7 @@ EXPORTED_SYMBOLS = (
     "gqa_decode_sliding", "gqa_decode_global", "gqa_decode_sliding_paged",
     "gqa_decode_global_paged", "gqa_decode_workspace_bytes", "gqa_decode_plan",
     "gqa_decode_constants", "gqa_status_str", "gqa_profile_begin", "gqa_profile_read",
+    "gqa_hbm_read_probe", "gqa_hbm_copy_probe",
 )
 
 
@@ -58,6 +59,10 @@ def library():
     lib.gqa_profile_begin.restype = ctypes.c_int
     lib.gqa_profile_read.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), i32]
     lib.gqa_profile_read.restype = ctypes.c_int
+    lib.gqa_hbm_read_probe.argtypes = [p, sz, p, p]
+    lib.gqa_hbm_read_probe.restype = ctypes.c_int
+    lib.gqa_hbm_copy_probe.argtypes = [p, p, sz, p]
+    lib.gqa_hbm_copy_probe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -110,6 +115,26 @@ def profile_read() -> dict:
         for ki, kname in enumerate(("split", "combine")):
             out[(vname, kname)] = (counts[2 * vi + ki], ms[2 * vi + ki])
     return out
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Plain read stream over src (measurement only)."""
+    nbytes = src.numel() * src.element_size()
+    rc = library().gqa_hbm_read_probe(_dev(src, "src"), nbytes, _dev(sink, "sink"),
+                                      _stream(stream, src.device))
+    if rc:
+        raise GqaError("gqa_hbm_read_probe", rc)
+
+
+def hbm_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Plain copy src -> dst (measurement only)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    rc = library().gqa_hbm_copy_probe(_dev(src, "src"), _dev(dst, "dst"), nbytes,
+                                      _stream(stream, src.device))
+    if rc:
+        raise GqaError("gqa_hbm_copy_probe", rc)
 
 
 def _dtype_code(t: torch.Tensor) -> int:

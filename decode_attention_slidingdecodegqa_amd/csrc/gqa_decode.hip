@@ -546,6 +546,53 @@ __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   }
 }
 
+// ------------------------------------------------------- measurement kernels
+// Not part of the attention path: a plain read stream and a plain copy of a
+// known byte count, used to measure the sustainable HBM read rate of the part
+// and to calibrate a profiler's byte counters against the split kernels.  Each
+// wave moves 8 KiB per iteration in 16-byte lanes (1 KiB contiguous per
+// instruction).
+
+constexpr int kProbeUnroll = 8;
+
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* p, size_t n, unsigned* sink) {
+  const size_t lane = threadIdx.x & 63;
+  const size_t wave = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6;
+  const size_t n_waves = ((size_t)gridDim.x * blockDim.x) >> 6;
+  unsigned acc = 0;
+  for (size_t base = wave * 64 * kProbeUnroll; base < n; base += n_waves * 64 * kProbeUnroll) {
+    u32x4 x[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const size_t i = base + (size_t)u * 64 + lane;
+      x[u] = i < n ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+  }
+  // data dependence on every load without a store per thread
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(256) void hbm_copy_kernel(const u32x4* src, u32x4* dst, size_t n) {
+  const size_t lane = threadIdx.x & 63;
+  const size_t wave = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6;
+  const size_t n_waves = ((size_t)gridDim.x * blockDim.x) >> 6;
+  for (size_t base = wave * 64 * kProbeUnroll; base < n; base += n_waves * 64 * kProbeUnroll) {
+    u32x4 x[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const size_t i = base + (size_t)u * 64 + lane;
+      if (i < n) x[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const size_t i = base + (size_t)u * 64 + lane;
+      if (i < n) dst[i] = x[u];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Plan {
@@ -790,6 +837,24 @@ const char* gqa_status_str(int32_t status) {
     case GQA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+int gqa_hbm_read_probe(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return GQA_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return GQA_ERR_SHAPE;
+  if (!aligned16(src)) return GQA_ERR_ALIGN;
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(2048), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, static_cast<unsigned*>(sink));
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return GQA_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return GQA_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return GQA_ERR_ALIGN;
+  hipLaunchKernelGGL(hbm_copy_kernel, dim3(2048), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 int gqa_profile_begin(int32_t capacity) {

@@ -126,6 +126,16 @@ int gqa_decode_constants(int32_t variant, int32_t* heads, int32_t* kv_heads, int
 /* Static description of a status code. */
 const char* gqa_status_str(int32_t status);
 
+/* Measurement utilities, not part of the attention path: a plain read stream
+ * of `bytes` bytes from `src` (non-temporal 16-byte loads, 1 KiB contiguous
+ * per wave instruction; `sink` is a 4-byte device word the kernel may write)
+ * and a plain copy of `bytes` bytes from `src` to `dst`.  They measure the
+ * sustainable HBM rate and calibrate a profiler's byte counters.  bytes must
+ * be a positive multiple of 16 and the pointers 16-byte aligned device
+ * memory; asynchronous on `stream`.  Returns GQA_OK or a negative status. */
+int gqa_hbm_read_probe(const void* src, size_t bytes, void* sink, void* stream);
+int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Launch timing for measurement: while enabled, every kernel the library
  * launches is bracketed by HIP events recorded on its stream (at most
  * `capacity` launches are kept).  gqa_profile_read synchronises those events

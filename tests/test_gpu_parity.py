@@ -180,6 +180,22 @@ def test_profile_hooks_count_launches():
     assert res[("sliding", "split")][0] == 0
 
 
+def test_measurement_probes():
+    src = torch.rand(1 << 20, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    gqa.hbm_read_probe(src, sink)
+    gqa.hbm_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    # a size that is not a multiple of the wave stride
+    s2 = torch.rand(1000 * 4 + 4, device="cuda")
+    d2 = torch.zeros_like(s2)
+    gqa.hbm_copy_probe(s2, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, d2)
+
+
 # --------------------------------------------------------------- full-size workloads
 
 def _sample_rows(case, n_seq, seed):
