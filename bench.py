@@ -215,8 +215,10 @@ def main():
         n, t = prof[key]
         return t / n if n else 0.0
 
-    sl_ms = avg(("sliding", "split")) + avg(("sliding", "combine"))
-    gl_split_ms = avg(("global", "split"))
+    sl_main_ms = avg(("sliding", "main"))
+    sl_comb_ms = avg(("sliding", "combine"))
+    sl_ms = sl_main_ms + sl_comb_ms
+    gl_split_ms = avg(("global", "main"))
     gl_comb_ms = avg(("global", "combine"))
     gl_ms = gl_split_ms + gl_comb_ms
     total_bytes = sl_bytes + gl_bytes
@@ -224,29 +226,31 @@ def main():
     achieved = gl_bytes / (gl_split_ms * 1e-3) / 1e9
     traffic = read_traffic()
 
-    n_split_gl, tps_gl = gqa.gqa_decode_plan("global", gl.B, gl.cap)
-    n_split_sl, tps_sl = gqa.gqa_decode_plan("sliding", sl.B, sl.cap)
+    plan_gl = gqa.gqa_decode_plan("global", gl.B, gl.cap)
+    plan_sl = gqa.gqa_decode_plan("sliding", sl.B, sl.cap)
     config = {
         "workload": f"{SLIDING} + {GLOBAL}",
         "sliding": {
             "B": sl.B, "S_max": sl.cap, "kv_heads": 16, "head_dim": 256, "window": 1024,
             "cache": "contiguous", "kv_bytes_per_call": sl_bytes,
             "us_per_call": round(sl_ms * 1e3, 2),
+            "main_kernel_us": round(sl_main_ms * 1e3, 2),
+            "combine_kernel_us": round(sl_comb_ms * 1e3, 2),
             "kv_GBps": round(sl_bytes / (sl_ms * 1e-3) / 1e9, 1) if sl_ms else None,
             "frac_of_hbm_peak": round(sl_bytes / (sl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
             if sl_ms else None,
-            "n_split": n_split_sl, "tiles_per_split": tps_sl,
+            "plan": plan_sl,
         },
         "global": {
             "B": gl.B, "max_pages": gl.block_table.shape[1], "num_pages": gl.k.shape[0],
             "kv_heads": 4, "head_dim": 512, "cache": "paged16", "kv_bytes_per_call": gl_bytes,
             "us_per_call": round(gl_ms * 1e3, 2),
-            "split_kernel_us": round(gl_split_ms * 1e3, 2),
+            "main_kernel_us": round(gl_split_ms * 1e3, 2),
             "combine_kernel_us": round(gl_comb_ms * 1e3, 2),
             "kv_GBps": round(gl_bytes / (gl_ms * 1e-3) / 1e9, 1) if gl_ms else None,
             "frac_of_hbm_peak": round(gl_bytes / (gl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
             if gl_ms else None,
-            "n_split": n_split_gl, "tiles_per_split": tps_gl,
+            "plan": plan_gl,
         },
     }
     line = {
@@ -264,7 +268,7 @@ def main():
         "data": "synthetic (seeded; unit-RMS values, RMS-normed weighted q/k)",
         "config": config,
         "roofline": {
-            "kernel": "gqa_split_kernel<4,512,paged,bf16> (decodeGQA, B=32 paged)",
+            "kernel": "gqa_stream_kernel<4,512,paged,bf16> (decodeGQA, B=32 paged)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

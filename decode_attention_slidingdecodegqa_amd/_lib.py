@@ -49,7 +49,7 @@ def library():
         f.argtypes, f.restype = args, ctypes.c_int
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32]
     lib.gqa_decode_workspace_bytes.restype = sz
-    lib.gqa_decode_plan.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.gqa_decode_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
     lib.gqa_decode_plan.restype = ctypes.c_int
     lib.gqa_decode_constants.argtypes = [i32] + [ctypes.POINTER(i32)] * 5
     lib.gqa_decode_constants.restype = ctypes.c_int
@@ -87,13 +87,18 @@ def gqa_decode_workspace_bytes(variant, B: int, capacity: int) -> int:
     return int(library().gqa_decode_workspace_bytes(_variant(variant), int(B), int(capacity)))
 
 
-def gqa_decode_plan(variant, B: int, capacity: int) -> tuple[int, int]:
-    n, t = ctypes.c_int32(), ctypes.c_int32()
-    rc = library().gqa_decode_plan(_variant(variant), int(B), int(capacity), ctypes.byref(n),
-                                   ctypes.byref(t))
+GQA_MODE_UNIT, GQA_MODE_STREAM = 0, 1
+
+
+def gqa_decode_plan(variant, B: int, capacity: int) -> dict:
+    """Launch plan: {'mode': 'unit'|'stream', 'waves': W, 'slots': workspace slots}."""
+    mode, n, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = library().gqa_decode_plan(_variant(variant), int(B), int(capacity), ctypes.byref(mode),
+                                   ctypes.byref(n), ctypes.byref(t))
     if rc:
         raise GqaError("gqa_decode_plan", rc)
-    return n.value, t.value
+    return {"mode": "unit" if mode.value == GQA_MODE_UNIT else "stream", "waves": n.value,
+            "slots": t.value}
 
 
 def profile_begin(capacity: int) -> None:
@@ -104,7 +109,7 @@ def profile_begin(capacity: int) -> None:
 
 def profile_read() -> dict:
     """{(variant, kernel): (launches, total_ms)} for variant in sliding/global and
-    kernel in split/combine."""
+    kernel in main/combine (the stream kernel and the split combine)."""
     counts = (ctypes.c_int32 * 4)()
     ms = (ctypes.c_double * 4)()
     rc = library().gqa_profile_read(counts, ms, 4)
@@ -112,7 +117,7 @@ def profile_read() -> dict:
         raise GqaError("gqa_profile_read", rc)
     out = {}
     for vi, vname in enumerate(("sliding", "global")):
-        for ki, kname in enumerate(("split", "combine")):
+        for ki, kname in enumerate(("main", "combine")):
             out[(vname, kname)] = (counts[2 * vi + ki], ms[2 * vi + ki])
     return out
 

@@ -7,32 +7,34 @@
 // [B,S,kv,D] cache or on a paged cache of 16-position pages (the "At a glance"
 // table's Shape domain row).  The C ABI is declared in include/gqa_decode.h.
 //
-// Method: flash-decoding.  The attended positions of one (sequence, kv head)
-// pair -- a "unit" -- are cut into tiles of 16 positions (one page).  A tile
-// is consumed by one wave64 with every query head of the GQA group at once:
+// Method: flash-decoding with an exactly balanced ("stream-K") partition.
 //
-//   QK^T  v_mfma_f32_16x16x32_bf16 (or 16x16x4_f32): A = 16 key rows of the
-//         tile, B = the group's query heads (padded to 16 columns with zeros).
-//         The reduction index may be any permutation of d shared by A and B,
-//         so each lane loads whole 16-byte chunks of one key row straight
-//         from HBM in the order the instruction wants them.
-//   softmax online, in fp32: running max m and sum l per head, base-2
-//         exponentials of (z - m) * log2(e).  The logit accumulator layout
-//         (lane = head column, 4 consecutive positions per lane) is exactly
+//   Work.  A unit is one (sequence b, kv head g); its attended positions
+//   [lo, L) are cut into 16-position tiles (a tile is one page).  All tiles of
+//   all units form one sequence, unit-major.  A fixed number W of persistent
+//   waves each take an equal contiguous slice of it, whatever the mix of
+//   sequence lengths, and carry their softmax state across the slice.  When a
+//   slice leaves a unit, the wave flushes that unit's partial (O, m, l) to
+//   workspace slot unit + wave, or writes o itself when its slice held the
+//   whole unit; a combine kernel merges the 1..n partials of split units.
+//
+//   Tile.  One wave64 consumes a tile with every query head of the GQA group:
+//   QK^T  v_mfma_f32_16x16x32_bf16 (16x16x4_f32 for f32): A = the 16 key rows,
+//         B = the group's query heads padded to 16 zero columns.  The
+//         reduction index may be any permutation of d shared by A and B, so
+//         each lane loads whole 16-byte chunks of one key row straight into
+//         the operand registers.
+//   softmax online, fp32: base-2 exponentials of (z - m) * log2(e).  The logit
+//         accumulator layout (lane = head column, 4 consecutive positions) is
 //         the B operand layout of the PV instruction, so P never moves.
-//   PV    v_mfma_f32_16x16x16_bf16 (or 16x16x4_f32) computing O^T = V^T P^T:
-//         A = V^T, built by transposing in registers the 4 rows x 8 columns a
-//         lane loads with 16-byte loads (one v_perm_b32 per output dword).
-//
-// The accumulator keeps O^T, so the per-head rescale factor of the online
-// softmax is a per-lane scalar.  Four waves of a work-group take interleaved
-// tiles of one split and merge their (m, l, O) through LDS; when the host
-// plans more than one split per unit, each work-group stores its partial
-// (O, m, l) in the fp32 workspace and a combine kernel merges the splits.
+//   PV    v_mfma_f32_16x16x16_bf16 (16x16x4_f32): O^T = V^T P^T with V^T built
+//         by transposing in registers the 4 rows x 8 columns a lane loads.
+//   The accumulator holds O^T, so the per-head rescale is a per-lane scalar.
 //
 // Every K/V byte of the attended range is read from HBM exactly once; no byte
-// outside it is read (masked rows are never loaded, so NaN or stale data in
-// unused cache space cannot leak into the result).
+// outside it is read (rows outside [lo, L) are clamped onto attended rows of
+// the same tile and dropped through -inf logits, so NaN or stale data in
+// unused cache space cannot reach the result).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,7 +48,7 @@ namespace {
 constexpr int kHeads = 32;
 constexpr int kPage = 16;
 constexpr int kTile = 16;  // positions per tile: one page
-constexpr int kWaves = 4;  // waves per work-group of the split kernel
+constexpr int kWaves = 4;  // waves per work-group
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxBatch = 256;
 constexpr int kMaxSeq = 262144;
@@ -55,14 +57,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // raise the softmax reference max only when a tile exceeds it by more than
 // this (natural-log units): weights stay below e^8
 constexpr float kRescaleGap = 8.0f;
-
-// split planner: aim at ~8 work-groups per CU of a 256-CU part, with splits of
-// 4..128 tiles (64..2048 positions)
-constexpr long kTargetGroups = 2048;
-constexpr int kMinTilesPerSplit = 4;
-constexpr int kMaxTilesPerSplit = 128;
+// persistent waves per launch: the 1024 SIMDs of a 256-CU part at the
+// occupancy of the variant's bf16 kernel (2 waves/SIMD sliding, 1 global)
+constexpr int kWavesSliding = 2048;
+constexpr int kWavesGlobal = 1024;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -81,43 +82,46 @@ struct Elem<false> {
   static constexpr int bytes = 4;
 };
 
-struct SplitArgs {
+struct KernelArgs {
   const char* q;
   const char* k;
   const char* v;
   const int32_t* seq_lens;
   const int32_t* block_table;
   char* o;
-  float* ws_ml;   // [unit][split][G][2]  (m, l)
-  float* ws_acc;  // [unit][split][G][D]
+  int32_t* prefix;  // [B+1] flattened tile index of each sequence's first unit
+  float* ws_ml;     // [slot][G][2]  (m, l)
+  float* ws_acc;    // [slot][G][D]
+  int32_t B;
   int32_t cap;
   int32_t max_pages;
   int32_t num_pages;
   int32_t window;
-  int32_t n_split;
-  int32_t tps;  // tiles per split
+  int32_t n_waves;
 };
 
-struct Range {
-  int lo, L;  // attended positions [lo, L)
-  int t0, t1; // tiles [t0, t1) that hold them
+// Attended range of one sequence: positions [lo, L), tiles [t0, t0 + n).
+struct SeqRange {
+  int lo, L, t0, n;
 };
 
-// The attended range of sequence b; shared by the split and combine kernels so
-// that both cut it identically.
-__device__ inline Range unit_range(const int32_t* seq_lens, int b, int cap, int window) {
-  int L = seq_lens[b];
-  L = L < cap ? L : cap;
-  Range r;
+__device__ inline SeqRange seq_range(int L_raw, int cap, int window) {
+  SeqRange s;
+  const int L = L_raw < cap ? L_raw : cap;
   if (L <= 0) {
-    r.lo = r.L = r.t0 = r.t1 = 0;
-    return r;
+    s.lo = s.L = s.t0 = s.n = 0;
+    return s;
   }
-  r.L = L;
-  r.lo = (window > 0 && L > window) ? L - window : 0;
-  r.t0 = r.lo / kTile;
-  r.t1 = (L + kTile - 1) / kTile;
-  return r;
+  s.L = L;
+  s.lo = (window > 0 && L > window) ? L - window : 0;
+  s.t0 = s.lo / kTile;
+  s.n = (L + kTile - 1) / kTile - s.t0;
+  return s;
+}
+
+// Wave whose slice holds flattened tile t: slice w is [w*T/W, (w+1)*T/W).
+__device__ inline int wave_of(long t, long T, int W) {
+  return (int)(((t + 1) * W - 1) / T);
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -149,7 +153,11 @@ __device__ inline float chunk_f32(const u32x4& c, int e) {
   return __builtin_bit_cast(float, x);
 }
 
-// Store 4E consecutive fp32 values as E-sized output chunks (16 bytes each).
+__device__ inline int pick4(int a0, int a1, int a2, int a3, int i) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+
+// Store n consecutive fp32 values as 16-byte output chunks.
 template <bool BF16>
 __device__ inline void store_run(char* dst, const float* v, int n) {
   if constexpr (BF16) {
@@ -167,149 +175,154 @@ __device__ inline void store_run(char* dst, const float* v, int n) {
   }
 }
 
-// Waves per SIMD the split kernel is compiled for: the sliding bf16 kernel fits
-// two (<= 256 registers), the others need one.
+// Waves per SIMD the main kernels are compiled for: the sliding bf16 kernels
+// fit two (<= 256 registers), the others need one.
 template <int KV, bool BF16>
-constexpr int split_waves_per_simd() {
+constexpr int main_waves_per_simd() {
   return (KV == 16 && BF16) ? 2 : 1;
 }
 
+// Compile-time geometry of one variant.
+template <int KV, int D, bool BF16>
+struct Geo {
+  static constexpr int G = kHeads / KV;             // query heads per kv head
+  static constexpr int E = Elem<BF16>::E;           // elements per 16-byte chunk
+  static constexpr int EB = Elem<BF16>::bytes;      // bytes per element
+  static constexpr int ROW = D * EB;                // bytes of one head row
+  static constexpr size_t POS = (size_t)KV * D * EB;  // bytes between positions
+  static constexpr int NCH = D / E;                 // 16-byte chunks per row
+  static constexpr int KCH = NCH / 4;               // key chunks per lane (chunk 4t+j)
+  static constexpr int VBLK = NCH / 16;             // value chunks per lane and row (r+16*blk)
+  static constexpr int RUN = 4 * E;                 // contiguous d values per lane and blk
+  static constexpr int QPL = (G * NCH + 63) / 64;   // query chunks per lane when staging
+};
+
+// The calling wave's online-softmax state for the heads of one unit.
+template <int KV, int D, bool BF16>
+struct WaveState {
+  using Gm = Geo<KV, D, BF16>;
+  f32x4 acc[Gm::VBLK][Gm::E];  // O^T: lane (r, j) holds head r, d = 16E*blk + 4E*j + E*i + e
+  float m;                     // reference max of head r (equal on the 4 lanes of a column)
+  float l;                     // this lane's share of the sum of weights
+};
+
+// Accumulates into st the tiles k_begin, k_begin + step, ... (< k_end) of unit
+// (b, g), whose attended range is sr, with the calling wave.  myq is the wave's
+// LDS slice for the unit's query heads.
 template <int KV, int D, bool PAGED, bool BF16>
-__global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void gqa_split_kernel(
-    SplitArgs a) {
-  constexpr int G = kHeads / KV;  // query heads per kv head
-  constexpr int E = Elem<BF16>::E;
-  constexpr int EB = Elem<BF16>::bytes;
-  constexpr int ROW = D * EB;                    // bytes of one head row
-  constexpr size_t POS = (size_t)KV * D * EB;    // bytes between positions
-  constexpr int NCH = D / E;                     // 16-byte chunks per row
-  constexpr int KCH = NCH / 4;                   // key chunks per lane (chunk 4t+j)
-  constexpr int VBLK = NCH / 16;                 // value chunks per lane and row (r+16*blk)
-  constexpr int RUN = 4 * E;                     // contiguous d values per lane and blk
-  constexpr int LROW = D + 4;                    // padded LDS row (floats)
-
-  __shared__ float s_acc[(kWaves - 1) * G * LROW];
-  __shared__ float s_m[(kWaves - 1) * G];
-  __shared__ float s_l[(kWaves - 1) * G];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+__device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int g,
+                                                 const SeqRange& sr, int k_begin, int k_end,
+                                                 int step, u32x4* myq,
+                                                 WaveState<KV, D, BF16>& st) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
+                VBLK = Gm::VBLK, QPL = Gm::QPL;
+  constexpr size_t POS = Gm::POS;
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15;  // row (A) / column (B, C) index of the 16x16 tiles
   const int j = lane >> 4;  // k-group of the operands, row-group of C
-  const int split = blockIdx.x % a.n_split;
-  const int unit = blockIdx.x / a.n_split;
-  const int b = unit / KV;
-  const int g = unit % KV;
-  const bool direct = a.n_split == 1;
 
-  const Range rg = unit_range(a.seq_lens, b, a.cap, a.window);
-  const int wg_t0 = rg.t0 + split * a.tps;
-  const int wg_t1 = min(rg.t1, wg_t0 + a.tps);
-
-  if (wg_t0 >= wg_t1) {
-    // nothing attended in this split
-    if (direct) {
-      for (int c = tid; c < G * NCH; c += kThreads) {
-        char* dst = a.o + ((size_t)b * kHeads + g * G + c / NCH) * ROW + (c % NCH) * 16;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
-      }
-    } else if (tid < G) {
-      float* ml = a.ws_ml + (((size_t)unit * a.n_split + split) * G + tid) * 2;
-      ml[0] = -INFINITY;
-      ml[1] = 0.f;
-    }
-    return;
-  }
-
-  // query heads of the group as the B operand of QK^T (columns >= G are zero)
-  u32x4 qreg[KCH];
-  {
-    const char* qrow = a.q + ((size_t)b * kHeads + g * G + (r < G ? r : 0)) * ROW;
 #pragma unroll
-    for (int t = 0; t < KCH; ++t) {
-      const u32x4 x = load16(qrow + (4 * t + j) * 16);
-      qreg[t] = r < G ? x : u32x4{0u, 0u, 0u, 0u};
+  for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The reference max is raised only when a tile's max exceeds it by more
+  // than kRescaleGap, so weights stay below e^kRescaleGap and the O/l rescale
+  // runs a few times per unit instead of every tile; the softmax is the same.
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const int n_it = k_end > k_begin ? (k_end - k_begin + step - 1) / step : 0;
+  if (n_it == 0) return;
+
+  // The group's query heads live in the wave's LDS slice (row h = head g*G+h,
+  // NCH chunks); QK^T reads them back per tile as the B operand, columns >= G
+  // being zero.  Their global loads go first and the LDS store waits for the
+  // first tile's K/V loads to be in flight, so the two latencies overlap.
+  u32x4 qstage[QPL];
+  {
+    const char* qsrc = a.q + ((size_t)b * kHeads + g * G) * ROW;
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < G * NCH) qstage[i] = load16(qsrc + (size_t)c * 16);
     }
   }
+  const u32x4* qrow = myq + (r < G ? r : 0) * NCH;
 
-  // this wave takes tiles wg_t0 + wave + 4*i, i < n_mine; lane i holds the
-  // physical page of its i-th tile (one vector load instead of one dependent
-  // scalar load per tile)
-  const int first = wg_t0 + wave;
-  const int n_mine = first < wg_t1 ? (wg_t1 - first + kWaves - 1) / kWaves : 0;
-  int pages = 0;
+  // Physical pages of iterations it0 + lane (cur) and it0 + 64 + lane (nxt);
+  // block-table entries of pages without an attended position are never read.
+  const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages + sr.t0 : nullptr;
+  int it0 = 0;
+  int pg_cur = 0, pg_nxt = 0;
   if constexpr (PAGED) {
-    if (lane < n_mine) pages = a.block_table[(size_t)b * a.max_pages + first + kWaves * lane];
+    if (lane < n_it) pg_cur = bt[k_begin + step * lane];
+    if (64 + lane < n_it) pg_nxt = bt[k_begin + step * (64 + lane)];
   }
 
   // Per-tile addressing.  Rows outside [lo, L) are clamped onto the nearest
   // attended row of the same tile: every load is unconditional yet never
   // leaves the attended range; the clamped duplicates are dropped below by
-  // setting their logits to -inf (so their softmax weight is exactly 0).
+  // -inf logits (their softmax weight is exactly 0).
   struct TileAt {
     const char* kb;
     const char* vb;
     int pos0;
     bool ok;  // page id inside the pool
   };
-  auto tile_at = [&](int i) {
-    TileAt t;
-    const int tile = first + kWaves * i;
-    t.pos0 = tile * kTile;
+  auto tile_at = [&](int it) {
+    TileAt ta;
+    ta.pos0 = (sr.t0 + k_begin + step * it) * kTile;
     size_t off;
     if constexpr (PAGED) {
-      const int page = __builtin_amdgcn_readlane(pages, i);
-      t.ok = page >= 0 && page < a.num_pages;
-      off = ((size_t)(t.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+      const int i = it - it0;
+      const int page = i < 64 ? __builtin_amdgcn_readlane(pg_cur, i)
+                              : __builtin_amdgcn_readlane(pg_nxt, i - 64);
+      ta.ok = page >= 0 && page < a.num_pages;
+      off = ((size_t)(ta.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
     } else {
-      t.ok = true;
-      off = (((size_t)b * a.cap + t.pos0) * KV + g) * (size_t)ROW;
+      ta.ok = true;
+      off = (((size_t)b * a.cap + ta.pos0) * KV + g) * (size_t)ROW;
     }
-    t.kb = a.k + off;
-    t.vb = a.v + off;
-    return t;
+    ta.kb = a.k + off;
+    ta.vb = a.v + off;
+    return ta;
   };
   auto clamp_row = [&](int pos0, int row) {
-    const int p = min(max(pos0 + row, rg.lo), rg.L - 1);
+    const int p = min(max(pos0 + row, sr.lo), sr.L - 1);
     return p - pos0;
   };
 
-  u32x4 kreg[KCH];       // key row r of the tile, chunks 4t+j
-  u32x4 vreg[4][VBLK];   // value rows 4j+i of the tile, chunks r+16*blk
-  auto load_k = [&](const TileAt& t) {
-    const char* row = t.kb + (size_t)clamp_row(t.pos0, r) * POS;
+  u32x4 kreg[KCH];      // key row r of the tile, chunks 4t+j
+  u32x4 vreg[4][VBLK];  // value rows 4j+i of the tile, chunks r+16*blk
+  auto load_k = [&](const TileAt& ta) {
+    const char* row = ta.kb + (size_t)clamp_row(ta.pos0, r) * POS;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) kreg[c] = load16(row + (4 * c + j) * 16);
   };
-  auto load_v = [&](const TileAt& t) {
+  auto load_v = [&](const TileAt& ta) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const char* row = t.vb + (size_t)clamp_row(t.pos0, 4 * j + i) * POS;
+      const char* row = ta.vb + (size_t)clamp_row(ta.pos0, 4 * j + i) * POS;
 #pragma unroll
-      for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16_stream(row + (r + 16 * blk) * 16);
+      for (int blk = 0; blk < VBLK; ++blk)
+        vreg[i][blk] = load16_stream(row + (r + 16 * blk) * 16);
     }
   };
 
-  f32x4 acc[VBLK][E];
-#pragma unroll
-  for (int blk = 0; blk < VBLK; ++blk)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Reference max of head r (equal on the 4 lanes of a column).  It is raised
-  // only when a tile's max exceeds it by more than kRescaleGap, so weights
-  // stay below e^kRescaleGap and the O/l rescale runs a few times per wave
-  // instead of every tile; the result is the same softmax either way.
-  float m = -INFINITY;
-  float l = 0.f;  // this lane's share of the sum of weights
-
   TileAt cur = tile_at(0);
-  if (n_mine > 0) {
-    load_k(cur);
-    load_v(cur);
+  load_k(cur);
+  load_v(cur);
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < G * NCH) myq[c] = qstage[i];
   }
-  for (int it = 0; it < n_mine; ++it) {
-    const bool more = it + 1 < n_mine;
+  // one wave writes and reads its own slice: a wavefront-scope fence orders them
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  for (int it = 0; it < n_it; ++it) {
+    const bool more = it + 1 < n_it;
     const TileAt nxt = more ? tile_at(it + 1) : cur;
 
     // logits z[pos 4j+i][head r]
@@ -318,22 +331,24 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
       f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF16) {
 #pragma unroll
-        for (int t = 0; t < KCH; t += 2) {
-          z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kreg[t]), __builtin_bit_cast(bf16x8, qreg[t]), z0, 0, 0, 0);
-          z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kreg[t + 1]), __builtin_bit_cast(bf16x8, qreg[t + 1]), z1,
-              0, 0, 0);
+        for (int c = 0; c < KCH; c += 2) {
+          const u32x4 q0 = r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 q1 = r < G ? qrow[4 * c + 4 + j] : u32x4{0u, 0u, 0u, 0u};
+          z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c]),
+                                                       __builtin_bit_cast(bf16x8, q0), z0, 0, 0, 0);
+          z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c + 1]),
+                                                       __builtin_bit_cast(bf16x8, q1), z1, 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < KCH; ++t) {
+        for (int c = 0; c < KCH; ++c) {
+          const u32x4 qc = r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
-            z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[t], e),
-                                                      chunk_f32(qreg[t], e), z0, 0, 0, 0);
-            z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[t], e + 1),
-                                                      chunk_f32(qreg[t], e + 1), z1, 0, 0, 0);
+            z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e), chunk_f32(qc, e), z0,
+                                                      0, 0, 0);
+            z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e + 1),
+                                                      chunk_f32(qc, e + 1), z1, 0, 0, 0);
           }
         }
       }
@@ -345,27 +360,27 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = cur.pos0 + 4 * j + i;
-      if (!(cur.ok && p >= rg.lo && p < rg.L)) z[i] = -INFINITY;
+      if (!(cur.ok && p >= sr.lo && p < sr.L)) z[i] = -INFINITY;
     }
 
     // online softmax (fp32)
     float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool grow = tmax > m + kRescaleGap;  // also when m = -inf and tmax is finite
+    const bool grow = tmax > st.m + kRescaleGap;  // also when m = -inf and tmax is finite
     if (__any(grow)) {
-      const float m_next = grow ? tmax : m;
-      const float alpha = exp2_fast((m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+      const float m_next = grow ? tmax : st.m;
+      const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
       if (grow) {
-        l *= alpha;
+        st.l *= alpha;
 #pragma unroll
         for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[blk][e] *= alpha;
+          for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
       }
-      m = m_next;
+      st.m = m_next;
     }
-    const float m_use = m == -INFINITY ? 0.f : m;
+    const float m_use = st.m == -INFINITY ? 0.f : st.m;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
@@ -374,7 +389,7 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
       unsigned pb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = bf16_bits(p[i]);
-      l += (bf16_value(pb[0]) + bf16_value(pb[1])) + (bf16_value(pb[2]) + bf16_value(pb[3]));
+      st.l += (bf16_value(pb[0]) + bf16_value(pb[1])) + (bf16_value(pb[2]) + bf16_value(pb[3]));
       const s16x4 pt =
           __builtin_bit_cast(s16x4, u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)});
 #pragma unroll
@@ -386,30 +401,224 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
           const unsigned lo = __builtin_amdgcn_perm(vreg[1][blk][dw], vreg[0][blk][dw], sel);
           const unsigned hi = __builtin_amdgcn_perm(vreg[3][blk][dw], vreg[2][blk][dw], sel);
           const s16x4 vt = __builtin_bit_cast(s16x4, u32x2{lo, hi});
-          acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, acc[blk][e], 0, 0, 0);
+          st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, st.acc[blk][e], 0, 0, 0);
         }
       }
     } else {
-      l += (p[0] + p[1]) + (p[2] + p[3]);
+      st.l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e), p[i],
-                                                               acc[blk][e], 0, 0, 0);
+            st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e), p[i],
+                                                                  st.acc[blk][e], 0, 0, 0);
     }
     // the value registers are free: fetch the next tile's values
     if (more) load_v(nxt);
+    if constexpr (PAGED) {
+      if (it + 1 - it0 == 64) {
+        it0 += 64;
+        pg_cur = pg_nxt;
+        pg_nxt = it0 + 64 + lane < n_it ? bt[k_begin + step * (it0 + 64 + lane)] : 0;
+      }
+    }
     cur = nxt;
   }
+  // the lane's share of l summed over the 4 lanes of its column
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+}
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+// Writes the wave's O row of head r (lane (r, j), r < G, owns the runs
+// d = 16E*blk + 4E*j + [0, 4E)) scaled by inv, in the output dtype.
+template <int KV, int D, bool BF16>
+__device__ __forceinline__ void store_o(const WaveState<KV, D, BF16>& st, char* o_row, float inv) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int E = Gm::E, EB = Gm::EB, VBLK = Gm::VBLK;
+  const int j = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int blk = 0; blk < VBLK; ++blk) {
+    char* dst = o_row + (size_t)(16 * E * blk + 4 * E * j) * EB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // the E values d = 16E*blk + 4E*j + E*i + e, e = 0..E-1: one 16-byte chunk
+      if constexpr (BF16) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = bf16_bits(st.acc[blk][2 * q][i] * inv) | (bf16_bits(st.acc[blk][2 * q + 1][i] * inv) << 16);
+        *reinterpret_cast<u32x4*>(dst + 16 * i) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 16 * i) =
+            f32x4{st.acc[blk][0][i], st.acc[blk][1][i], st.acc[blk][2][i], st.acc[blk][3][i]} * inv;
+      }
+    }
+  }
+}
 
-  // merge the four waves: lane (r, j) holds, for head r and each blk, the d
-  // values 16E*blk + 4E*j + E*i + e  (i = C row within the lane, e = instruction)
+// Writes the wave's unnormalised O row of head r as fp32 (same ownership).
+template <int KV, int D, bool BF16>
+__device__ __forceinline__ void store_partial(const WaveState<KV, D, BF16>& st, float* ws_row) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int E = Gm::E, VBLK = Gm::VBLK;
+  const int j = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int blk = 0; blk < VBLK; ++blk) {
+    float* dst = ws_row + 16 * E * blk + 4 * E * j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<f32x4*>(dst + E * i + e) =
+            f32x4{st.acc[blk][e][i], st.acc[blk][e + 1][i], st.acc[blk][e + 2][i], st.acc[blk][e + 3][i]};
+  }
+}
+
+// ---- stream kernel: W persistent waves, each an equal slice of all tiles
+template <int KV, int D, bool PAGED, bool BF16>
+__global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_stream_kernel(
+    KernelArgs a) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, ROW = Gm::ROW, NCH = Gm::NCH;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int w = blockIdx.x * kWaves + (threadIdx.x >> 6);  // this wave's slice
+
+  // ---- tile counts of every sequence and their prefix sums, once per
+  // work-group in LDS (wave 0: lane l takes sequences 4l .. 4l+3)
+  __shared__ int s_len[kMaxBatch];         // seq_lens
+  __shared__ int s_cnt[kMaxBatch];         // tiles per unit of the sequence
+  __shared__ int s_before[kMaxBatch + 1];  // tiles per unit summed over earlier sequences
+  __shared__ u32x4 s_q[kWaves][G * NCH];   // per-wave query heads of the current unit
+  if (threadIdx.x < 64) {
+    int cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      const int L = b < a.B ? a.seq_lens[b] : 0;
+      cnt[i] = seq_range(L, a.cap, a.window).n;
+      if (b < a.B) {
+        s_len[b] = L;
+        s_cnt[b] = cnt[i];
+      }
+    }
+    const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    int incl = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int run_b = incl - lsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      if (b < a.B) {
+        s_before[b] = run_b;
+        if (blockIdx.x == 0) a.prefix[b] = KV * run_b;
+      }
+      run_b += cnt[i];
+    }
+    if (lane == 63) {
+      s_before[a.B] = incl;
+      if (blockIdx.x == 0) a.prefix[a.B] = KV * incl;
+    }
+  }
+  __syncthreads();
+  const long T = (long)KV * s_before[a.B];  // tiles of all units
+
+  // ---- this wave's slice [s_begin, s_end) of the flattened tiles
+  const long s_begin = (long)w * T / a.n_waves;
+  const long s_end = (long)(w + 1) * T / a.n_waves;
+  if (s_begin >= s_end) return;
+
+  // the sequence holding s_begin: the last one whose first tile is <= s_begin
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = a.B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if ((long)KV * s_before[mid] <= s_begin) lo_b = mid;
+      else hi_b = mid - 1;
+    }
+    b = lo_b;
+  }
+  int n = s_cnt[b];
+  int g, kk0;
+  {
+    const int rel = (int)(s_begin - (long)KV * s_before[b]);
+    g = rel / n;
+    kk0 = rel % n;
+  }
+
+  WaveState<KV, D, BF16> st;
+  long t = s_begin;
+  while (t < s_end) {
+    // ---- one segment: tiles [k_begin, k_end) of unit (b, g)
+    const SeqRange sr = seq_range(s_len[b], a.cap, a.window);
+    const int k_begin = kk0;
+    const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
+    accumulate_tiles<KV, D, PAGED, BF16>(a, b, g, sr, k_begin, k_end, 1, s_q[threadIdx.x >> 6], st);
+
+    // the wave writes o when its slice holds the whole unit, else a partial
+    if (r < G) {
+      if (k_begin == 0 && k_end == n) {
+        const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+        store_o<KV, D, BF16>(st, a.o + ((size_t)b * kHeads + g * G + r) * ROW, inv);
+      } else {
+        const size_t slot = (size_t)(b * KV + g) + w;
+        store_partial<KV, D, BF16>(st, a.ws_acc + (slot * G + r) * D);
+        if (j == 0) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + r) * 2) = f32x2{st.m, st.l};
+      }
+    }
+
+    // ---- next unit (skipping sequences with nothing attended)
+    t += k_end - k_begin;
+    kk0 = 0;
+    if (++g == KV) {
+      g = 0;
+      do {
+        ++b;
+      } while (b < a.B && s_cnt[b] == 0);
+    }
+    if (t < s_end) n = s_cnt[b];
+  }
+}
+
+// ---- unit kernel: one work-group per unit (many short units); its four
+// waves take interleaved tiles and merge their states in LDS, then write o
+template <int KV, int D, bool PAGED, bool BF16>
+__global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_unit_kernel(
+    KernelArgs a) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, VBLK = Gm::VBLK;
+  constexpr int LROW = D + 4;  // padded LDS row (floats)
+  __shared__ u32x4 s_q[kWaves][G * NCH];
+  __shared__ float s_acc[(kWaves - 1) * G * LROW];
+  __shared__ float s_m[(kWaves - 1) * G];
+  __shared__ float s_l[(kWaves - 1) * G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int unit = blockIdx.x;
+  const int b = unit / KV;
+  const int g = unit % KV;
+  const SeqRange sr = seq_range(a.seq_lens[b], a.cap, a.window);
+  if (sr.n == 0) {  // nothing attended: zero rows
+    for (int c = threadIdx.x; c < G * NCH; c += kThreads)
+      *reinterpret_cast<u32x4*>(a.o + ((size_t)b * kHeads + g * G + c / NCH) * ROW + (c % NCH) * 16) =
+          u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+
+  WaveState<KV, D, BF16> st;
+  accumulate_tiles<KV, D, PAGED, BF16>(a, b, g, sr, wave, sr.n, kWaves, s_q[wave], st);
+
   if (wave > 0 && r < G) {
     float* dst = s_acc + ((wave - 1) * G + r) * LROW;
 #pragma unroll
@@ -417,81 +626,62 @@ __global__ __launch_bounds__(kThreads, (split_waves_per_simd<KV, BF16>())) void 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < E; ++e) dst[16 * E * blk + 4 * E * j + E * i + e] = acc[blk][e][i];
+        for (int e = 0; e < E; ++e) dst[16 * E * blk + 4 * E * j + E * i + e] = st.acc[blk][e][i];
     if (j == 0) {
-      s_m[(wave - 1) * G + r] = m;
-      s_l[(wave - 1) * G + r] = l;
+      s_m[(wave - 1) * G + r] = st.m;
+      s_l[(wave - 1) * G + r] = st.l;
     }
   }
   __syncthreads();
   if (wave != 0 || r >= G) return;
 
-  float M = m;
+  float M = st.m;
   float mw[kWaves - 1], lw[kWaves - 1];
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    mw[w] = s_m[w * G + r];
-    lw[w] = s_l[w * G + r];
-    M = fmaxf(M, mw[w]);
+  for (int v = 0; v < kWaves - 1; ++v) {
+    mw[v] = s_m[v * G + r];
+    lw[v] = s_l[v * G + r];
+    M = fmaxf(M, mw[v]);
   }
   const float Muse = M == -INFINITY ? 0.f : M;
-  const float sc0 = exp2_fast((m - Muse) * kLog2e);
+  const float sc0 = exp2_fast((st.m - Muse) * kLog2e);
   float sc[kWaves - 1];
-  float Lt = sc0 * l;
+  float Lt = sc0 * st.l;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    sc[w] = exp2_fast((mw[w] - Muse) * kLog2e);
-    Lt += sc[w] * lw[w];
+  for (int v = 0; v < kWaves - 1; ++v) {
+    sc[v] = exp2_fast((mw[v] - Muse) * kLog2e);
+    Lt += sc[v] * lw[v];
   }
-
-  const int head = g * G + r;
+  WaveState<KV, D, BF16> mg;
 #pragma unroll
-  for (int blk = 0; blk < VBLK; ++blk) {
-    const int d0 = 16 * E * blk + 4 * E * j;
-    float run[RUN];
+  for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < E; ++e) {
+      f32x4 x = sc0 * st.acc[blk][e];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int d = d0 + E * i + e;
-        float x = sc0 * acc[blk][e][i];
-#pragma unroll
-        for (int w = 0; w < kWaves - 1; ++w) x += sc[w] * s_acc[(w * G + r) * LROW + d];
-        run[E * i + e] = x;
+      for (int v = 0; v < kWaves - 1; ++v) {
+        const float* row = s_acc + (v * G + r) * LROW + 16 * E * blk + 4 * E * j + e;
+        x += sc[v] * f32x4{row[0], row[E], row[2 * E], row[3 * E]};
       }
-    if (direct) {
-      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-#pragma unroll
-      for (int c = 0; c < RUN; ++c) run[c] = Lt > 0.f ? run[c] * inv : 0.f;
-      store_run<BF16>(a.o + ((size_t)b * kHeads + head) * ROW + (size_t)d0 * EB, run, RUN);
-    } else {
-      float* dst = a.ws_acc + (((size_t)unit * a.n_split + split) * G + r) * D + d0;
-#pragma unroll
-      for (int c = 0; c < RUN; c += 4)
-        *reinterpret_cast<f32x4*>(dst + c) = f32x4{run[c], run[c + 1], run[c + 2], run[c + 3]};
+      mg.acc[blk][e] = x;
     }
-  }
-  if (!direct && j == 0) {
-    float* ml = a.ws_ml + (((size_t)unit * a.n_split + split) * G + r) * 2;
-    ml[0] = M;
-    ml[1] = Lt;
-  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  store_o<KV, D, BF16>(mg, a.o + ((size_t)b * kHeads + g * G + r) * ROW, inv);
 }
 
 struct CombineArgs {
-  const int32_t* seq_lens;
+  const int32_t* prefix;
   const float* ws_ml;
   const float* ws_acc;
   char* o;
-  int32_t cap;
-  int32_t window;
-  int32_t n_split;
-  int32_t tps;
+  int32_t B;
+  int32_t n_waves;
 };
 
 // One work-group per (sequence, query head); thread t owns d = 4t .. 4t+3.
-// Splits whose l is 0 hold no result (their workspace slots may be stale):
-// their weight is 0 and their values are selected away, never multiplied.
+// Merges the partials of a unit that several waves' slices share; a unit held
+// by one slice was written by its wave, and a sequence with nothing attended
+// gets a zero row.
 template <int KV, int D, bool BF16>
 __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   constexpr int G = kHeads / KV;
@@ -502,42 +692,55 @@ __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   const int g = h / G;
   const int hh = h % G;
   const int unit = b * KV + g;
-  const Range rg = unit_range(a.seq_lens, b, a.cap, a.window);
-  int n_used = rg.t1 > rg.t0 ? (rg.t1 - rg.t0 + a.tps - 1) / a.tps : 0;
-  n_used = n_used < a.n_split ? n_used : a.n_split;
-
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + (size_t)unit * a.n_split * G + hh;
-  float M = -INFINITY;
-  for (int s = 0; s < n_used; ++s) {
-    const f32x2 x = ml[(size_t)s * G];
-    if (x[1] > 0.f) M = fmaxf(M, x[0]);
-  }
   const int d = threadIdx.x * 4;
-  const float* accp = a.ws_acc + ((size_t)unit * a.n_split * G + hh) * D + d;
-  const size_t sstride = (size_t)G * D;
-  f32x4 A = {0.f, 0.f, 0.f, 0.f};
-  float Lt = 0.f;
-  for (int s0 = 0; s0 < n_used; s0 += U) {
-    f32x4 x[U];
-    float w[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u < n_used ? s0 + u : n_used - 1;
-      const f32x2 e = ml[(size_t)s * G];
-      const bool ok = s0 + u < n_used && e[1] > 0.f;
-      w[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
-      Lt += w[u] * (ok ? e[1] : 0.f);
-      x[u] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride);
-      x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) A += w[u] * x[u];
-  }
-  float run[4];
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  for (int c = 0; c < 4; ++c) run[c] = Lt > 0.f ? A[c] * inv : 0.f;
   char* dst = a.o + ((size_t)b * kHeads + h) * D * EB + (size_t)d * EB;
+
+  const int P0 = a.prefix[b];
+  const int n = (a.prefix[b + 1] - P0) / KV;
+  float run[4] = {0.f, 0.f, 0.f, 0.f};
+  if (n > 0) {
+    const long T = a.prefix[a.B];
+    const long s0 = P0 + (long)g * n;
+    const int wf = wave_of(s0, T, a.n_waves);
+    const int wl = wave_of(s0 + n - 1, T, a.n_waves);
+    if (wf == wl) return;  // written by the wave that held the whole unit
+    const int ns = wl - wf + 1;
+    const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + ((size_t)unit + wf) * G + hh;
+    const float* accp = a.ws_acc + (((size_t)unit + wf) * G + hh) * D + d;
+    const size_t sstride = (size_t)G * D;
+    // waves between wf and wl whose slices are empty (more waves than tiles)
+    // wrote nothing: their slots are skipped
+    auto holds = [&](int s) {
+      const long w = wf + s;
+      return (w + 1) * T / a.n_waves > w * T / a.n_waves;
+    };
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) {
+      if (!holds(s)) continue;
+      const f32x2 x = ml[(size_t)s * G];
+      if (x[1] > 0.f) M = fmaxf(M, x[0]);
+    }
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    float Lt = 0.f;
+    for (int s0u = 0; s0u < ns; s0u += U) {
+      f32x4 x[U];
+      float wgt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0u + u < ns ? s0u + u : ns - 1;
+        const f32x2 e = ml[(size_t)s * G];
+        const bool ok = s0u + u < ns && holds(s) && e[1] > 0.f;
+        wgt[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
+        Lt += wgt[u] * (ok ? e[1] : 0.f);
+        x[u] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride);
+        x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) A += wgt[u] * x[u];
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    for (int c = 0; c < 4; ++c) run[c] = Lt > 0.f ? A[c] * inv : 0.f;
+  }
   if constexpr (BF16) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{bf16_bits(run[0]) | (bf16_bits(run[1]) << 16),
                                            bf16_bits(run[2]) | (bf16_bits(run[3]) << 16)};
@@ -594,29 +797,42 @@ __global__ __launch_bounds__(256) void hbm_copy_kernel(const u32x4* src, u32x4* 
 }
 
 // ---------------------------------------------------------------- host side
-
-struct Plan {
-  int n_split;
-  int tps;
-};
+// ---------------------------------------------------------------- host side
 
 struct VariantInfo {
-  int KV, D, window;
+  int KV, D, window, waves;
 };
 
 inline bool variant_info(int variant, VariantInfo* vi) {
   if (variant == GQA_SLIDING) {
-    *vi = {16, 256, kSlidingWindow};
+    *vi = {16, 256, kSlidingWindow, kWavesSliding};
     return true;
   }
   if (variant == GQA_GLOBAL) {
-    *vi = {4, 512, 0};
+    *vi = {4, 512, 0, kWavesGlobal};
     return true;
   }
   return false;
 }
 
-int make_plan(int variant, int B, int cap, Plan* p) {
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Launch plan, a function of (variant, B, capacity) only.  Many short units
+// (at least kUnitModeMinUnits units of at most kUnitModeMaxTiles tiles) fill
+// the GPU one work-group per unit and need no workspace; otherwise the stream
+// partition runs with workspace
+//   [prefix: B+1 int32][ml: slots x G x 2 fp32][acc: slots x G x D fp32],
+// slots = B*KV + W (a slice's partial of unit u sits in slot u + wave).
+constexpr int kUnitModeMinUnits = 1024;
+constexpr int kUnitModeMaxTiles = 128;
+
+struct Plan {
+  int mode;  // GQA_MODE_UNIT or GQA_MODE_STREAM
+  int waves, slots;
+  size_t prefix, ml, acc, total;
+};
+
+int make_plan(int variant, int B, int cap, Plan* P) {
   VariantInfo vi;
   if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
   if (B < 1 || B > kMaxBatch || cap < 1 || cap > kMaxSeq) return GQA_ERR_SHAPE;
@@ -625,34 +841,22 @@ int make_plan(int variant, int B, int cap, Plan* p) {
     const int wt = (vi.window + kTile - 1) / kTile + 1;
     tiles_max = tiles_max < wt ? tiles_max : wt;
   }
-  const long units = (long)B * vi.KV;
-  long tps = ((long)tiles_max * units + kTargetGroups - 1) / kTargetGroups;
-  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
-  if (tps > kMaxTilesPerSplit) tps = kMaxTilesPerSplit;
-  long n_split = (tiles_max + tps - 1) / tps;
-  if (n_split <= 1) {
-    n_split = 1;
-    tps = tiles_max;
+  const int units = B * vi.KV;
+  *P = Plan{};
+  if (units >= kUnitModeMinUnits && tiles_max <= kUnitModeMaxTiles) {
+    P->mode = GQA_MODE_UNIT;
+    P->waves = units * kWaves;
+    return GQA_OK;
   }
-  p->n_split = (int)n_split;
-  p->tps = (int)tps;
+  const int G = kHeads / vi.KV;
+  P->mode = GQA_MODE_STREAM;
+  P->waves = vi.waves;
+  P->slots = units + vi.waves;
+  P->prefix = 0;
+  P->ml = align256((size_t)(B + 1) * sizeof(int32_t));
+  P->acc = P->ml + align256((size_t)P->slots * G * 2 * sizeof(float));
+  P->total = P->acc + (size_t)P->slots * G * vi.D * sizeof(float);
   return GQA_OK;
-}
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t ml_bytes(int variant, int B, const Plan& p) {
-  VariantInfo vi;
-  variant_info(variant, &vi);
-  return align256((size_t)B * vi.KV * p.n_split * (kHeads / vi.KV) * 2 * sizeof(float));
-}
-
-size_t workspace_bytes(int variant, int B, const Plan& p) {
-  if (p.n_split <= 1) return 0;
-  VariantInfo vi;
-  variant_info(variant, &vi);
-  return ml_bytes(variant, B, p) +
-         (size_t)B * vi.KV * p.n_split * (kHeads / vi.KV) * vi.D * sizeof(float);
 }
 
 // ---- launch timing (measurement only)
@@ -671,13 +875,18 @@ inline ProfRec* prof_slot(int kind) {
   return r;
 }
 
-typedef void (*SplitFn)(SplitArgs);
+typedef void (*MainFn)(KernelArgs);
 typedef void (*CombineFn)(CombineArgs);
 
 template <int KV, int D>
-SplitFn pick_split(bool paged, bool bf16) {
-  if (paged) return bf16 ? gqa_split_kernel<KV, D, true, true> : gqa_split_kernel<KV, D, true, false>;
-  return bf16 ? gqa_split_kernel<KV, D, false, true> : gqa_split_kernel<KV, D, false, false>;
+MainFn pick_main(bool unit_mode, bool paged, bool bf16) {
+  if (unit_mode) {
+    if (paged) return bf16 ? gqa_unit_kernel<KV, D, true, true> : gqa_unit_kernel<KV, D, true, false>;
+    return bf16 ? gqa_unit_kernel<KV, D, false, true> : gqa_unit_kernel<KV, D, false, false>;
+  }
+  if (paged)
+    return bf16 ? gqa_stream_kernel<KV, D, true, true> : gqa_stream_kernel<KV, D, true, false>;
+  return bf16 ? gqa_stream_kernel<KV, D, false, true> : gqa_stream_kernel<KV, D, false, false>;
 }
 
 template <int KV, int D>
@@ -708,57 +917,55 @@ int run(int variant, bool paged, const void* q, const void* k, const void* v,
   Plan plan;
   int rc = make_plan(variant, B, cap, &plan);
   if (rc) return rc;
-  const size_t need = workspace_bytes(variant, B, plan);
-  if (need > 0) {
-    if (!workspace || workspace_bytes_given < need) return GQA_ERR_WORKSPACE;
+  const bool unit_mode = plan.mode == GQA_MODE_UNIT;
+  if (!unit_mode) {
+    if (!workspace || workspace_bytes_given < plan.total) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_ALIGN;
   }
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const bool bf16 = dtype == GQA_BF16;
+  char* ws = static_cast<char*>(workspace);
 
-  SplitArgs sa;
-  sa.q = static_cast<const char*>(q);
-  sa.k = static_cast<const char*>(k);
-  sa.v = static_cast<const char*>(v);
-  sa.seq_lens = seq_lens;
-  sa.block_table = block_table;
-  sa.o = static_cast<char*>(o);
-  sa.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  sa.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes(variant, B, plan))
-                   : nullptr;
-  sa.cap = cap;
-  sa.max_pages = paged ? max_pages : 0;
-  sa.num_pages = paged ? num_pages : 0;
-  sa.window = vi.window;
-  sa.n_split = plan.n_split;
-  sa.tps = plan.tps;
+  KernelArgs ka;
+  ka.q = static_cast<const char*>(q);
+  ka.k = static_cast<const char*>(k);
+  ka.v = static_cast<const char*>(v);
+  ka.seq_lens = seq_lens;
+  ka.block_table = block_table;
+  ka.o = static_cast<char*>(o);
+  ka.prefix = unit_mode ? nullptr : reinterpret_cast<int32_t*>(ws + plan.prefix);
+  ka.ws_ml = unit_mode ? nullptr : reinterpret_cast<float*>(ws + plan.ml);
+  ka.ws_acc = unit_mode ? nullptr : reinterpret_cast<float*>(ws + plan.acc);
+  ka.B = B;
+  ka.cap = cap;
+  ka.max_pages = paged ? max_pages : 0;
+  ka.num_pages = paged ? num_pages : 0;
+  ka.window = vi.window;
+  ka.n_waves = plan.waves;
 
-  SplitFn split = variant == GQA_SLIDING ? pick_split<16, 256>(paged, bf16)
-                                         : pick_split<4, 512>(paged, bf16);
-  const unsigned groups = (unsigned)(B * vi.KV * plan.n_split);
+  MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256>(unit_mode, paged, bf16)
+                                          : pick_main<4, 512>(unit_mode, paged, bf16);
   ProfRec* pr = prof_slot(2 * variant);
   if (pr) hipEventRecord(pr->start, stream);
-  hipLaunchKernelGGL(split, dim3(groups), dim3(kThreads), 0, stream, sa);
+  hipLaunchKernelGGL(main_fn, dim3((unsigned)(plan.waves / kWaves)), dim3(kThreads), 0, stream, ka);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (pr) hipEventRecord(pr->stop, stream);
+  if (unit_mode) return GQA_OK;
 
-  if (plan.n_split > 1) {
-    CombineArgs ca;
-    ca.seq_lens = seq_lens;
-    ca.ws_ml = sa.ws_ml;
-    ca.ws_acc = sa.ws_acc;
-    ca.o = sa.o;
-    ca.cap = cap;
-    ca.window = vi.window;
-    ca.n_split = plan.n_split;
-    ca.tps = plan.tps;
-    CombineFn comb = variant == GQA_SLIDING ? pick_combine<16, 256>(bf16) : pick_combine<4, 512>(bf16);
-    ProfRec* pc = prof_slot(2 * variant + 1);
-    if (pc) hipEventRecord(pc->start, stream);
-    hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3((unsigned)(vi.D / 4)), 0, stream, ca);
-    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
-    if (pc) hipEventRecord(pc->stop, stream);
-  }
+  CombineArgs ca;
+  ca.prefix = ka.prefix;
+  ca.ws_ml = ka.ws_ml;
+  ca.ws_acc = ka.ws_acc;
+  ca.o = ka.o;
+  ca.B = B;
+  ca.n_waves = plan.waves;
+  CombineFn comb =
+      variant == GQA_SLIDING ? pick_combine<16, 256>(bf16) : pick_combine<4, 512>(bf16);
+  ProfRec* pc = prof_slot(2 * variant + 1);
+  if (pc) hipEventRecord(pc->start, stream);
+  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3((unsigned)(vi.D / 4)), 0, stream, ca);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  if (pc) hipEventRecord(pc->stop, stream);
   return GQA_OK;
 }
 
@@ -801,16 +1008,17 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity) {
   Plan p;
   if (make_plan(variant, B, capacity, &p)) return 0;
-  return workspace_bytes(variant, B, p);
+  return p.total;
 }
 
-int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* n_split,
-                    int32_t* tiles_per_split) {
+int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* mode,
+                    int32_t* n_waves, int32_t* n_slots) {
   Plan p;
   int rc = make_plan(variant, B, capacity, &p);
   if (rc) return rc;
-  if (n_split) *n_split = p.n_split;
-  if (tiles_per_split) *tiles_per_split = p.tps;
+  if (mode) *mode = p.mode;
+  if (n_waves) *n_waves = p.waves;
+  if (n_slots) *n_slots = p.slots;
   return GQA_OK;
 }
 

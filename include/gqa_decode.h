@@ -112,11 +112,19 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
  * the workspace may then be NULL.  Returns 0 for out-of-range arguments too. */
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity);
 
-/* The split-S plan the library uses for these arguments: number of splits per
- * (sequence, kv head) and 16-position tiles per split.  Returns GQA_OK or
- * GQA_ERR_SHAPE / GQA_ERR_DTYPE. */
-int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* n_split,
-                    int32_t* tiles_per_split);
+/* launch modes reported by gqa_decode_plan */
+enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1 };
+
+/* The launch plan for these arguments (a function of them alone).
+ * GQA_MODE_UNIT: one work-group of four waves per (sequence, kv head), used
+ *   when there are at least 1024 such units of at most 128 tiles of 16
+ *   positions; no workspace; *n_waves = 4 * units, *n_slots = 0.
+ * GQA_MODE_STREAM: *n_waves persistent waves each take an equal share of all
+ *   tiles, partials of units shared by several waves go to *n_slots workspace
+ *   slots, and a combine kernel merges them.
+ * Returns GQA_OK or GQA_ERR_SHAPE / GQA_ERR_DTYPE. */
+int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* mode,
+                    int32_t* n_waves, int32_t* n_slots);
 
 /* Compile-time constants of a variant (heads, kv heads, head dim, window, page).
  * window is 0 for decodeGQA.  Returns GQA_OK or GQA_ERR_DTYPE. */
@@ -140,7 +148,7 @@ int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
  * launches is bracketed by HIP events recorded on its stream (at most
  * `capacity` launches are kept).  gqa_profile_read synchronises those events
  * and reports, per kernel kind, the number of launches and their summed
- * duration in milliseconds (kind 2*variant: split kernel of that variant,
+ * duration in milliseconds (kind 2*variant: main kernel of that variant,
  * 2*variant+1: its combine kernel); it also disables recording and releases
  * the events.  Measurement only: not thread-safe, not for captured graphs. */
 int gqa_profile_begin(int32_t capacity);

@@ -56,31 +56,43 @@ def test_constants_match_pages(lib):
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 @pytest.mark.parametrize("B,cap", [(1, 1), (1, 262144), (4, 2048), (4, 4096), (32, 131072),
                                    (256, 8192), (256, 262144), (7, 33)])
-def test_plan_covers_every_tile(lib, variant, B, cap):
-    n_split, tps = gqa.gqa_decode_plan(variant, B, cap)
+def test_plan_and_workspace(lib, variant, B, cap):
+    plan = gqa.gqa_decode_plan(variant, B, cap)
     KV = 16 if variant == "sliding" else 4
+    G, D = 32 // KV, (256 if variant == "sliding" else 512)
     tiles = (cap + 15) // 16
     if variant == "sliding":
         tiles = min(tiles, 1024 // 16 + 1)
-    assert n_split >= 1 and tps >= 1
-    assert n_split * tps >= tiles                     # every attended tile has a split
-    assert (n_split - 1) * tps < tiles                # no split is empty for the longest unit
     ws = gqa.gqa_decode_workspace_bytes(variant, B, cap)
-    if n_split == 1:
+    if B * KV >= 1024 and tiles <= 128:
+        # many short units: one work-group of four waves per unit, no workspace
+        assert plan == {"mode": "unit", "waves": 4 * B * KV, "slots": 0}
         assert ws == 0
     else:
-        G, D = 32 // KV, (256 if variant == "sliding" else 512)
-        assert ws >= B * KV * n_split * G * (D + 2) * 4
+        assert plan["mode"] == "stream"
+        assert plan["waves"] == (2048 if variant == "sliding" else 1024)
+        assert plan["slots"] == B * KV + plan["waves"]   # slot u + w for every (unit, wave)
+        assert ws >= (B + 1) * 4 + plan["slots"] * G * (D + 2) * 4
 
 
-def test_plan_examples(lib):
-    # many (sequence, kv head) units: one split, the work-group covers the window
-    assert gqa.gqa_decode_plan("sliding", 256, 8192)[0] == 1
-    # few units over long caches: split-S
-    n, t = gqa.gqa_decode_plan("global", 32, 131072)
-    assert n > 1 and t * 16 <= 2048
-    n, t = gqa.gqa_decode_plan("global", 1, 262144)
-    assert n * 4 >= 256                               # at least one work-group per CU
+def test_plan_modes_of_the_workloads(lib):
+    assert gqa.gqa_decode_plan("sliding", 256, 8192)["mode"] == "unit"
+    assert gqa.gqa_decode_plan("global", 32, 131072)["mode"] == "stream"
+    assert gqa.gqa_decode_plan("global", 1, 262144)["mode"] == "stream"
+    assert gqa.gqa_decode_plan("sliding", 4, 2048)["mode"] == "stream"
+
+
+def test_slice_arithmetic_partitions_exactly():
+    # the stream partition: slice w = [w*T//W, (w+1)*T//W); the wave holding
+    # tile t is ((t+1)*W - 1)//T (the same integer formula runs on the device)
+    import random
+    rnd = random.Random(5)
+    for _ in range(2000):
+        T = rnd.randint(1, 10**7)
+        W = rnd.choice([1024, 2048, 7])
+        t = rnd.randrange(T)
+        w = ((t + 1) * W - 1) // T
+        assert w * T // W <= t < (w + 1) * T // W
 
 
 def test_bad_arguments_fail_before_launch(lib):

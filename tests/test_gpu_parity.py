@@ -55,6 +55,23 @@ def test_parity_batch_shapes(variant):
         assert err <= TOL["bf16"], (B, cap, err)
 
 
+UNIT_MODE = {"sliding": (64, 1104), "global": (256, 512)}  # B, capacity
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_parity_unit_mode(variant, dtype, paged):
+    # many short units: one work-group per (sequence, kv head)
+    B, cap = UNIT_MODE[variant]
+    assert gqa.gqa_decode_plan(variant, B, cap)["mode"] == "unit"
+    lens = synth.draw_seq_lens(("uniform", 1, cap), B, 7)
+    lens[0], lens[1], lens[2] = 1, cap, 0
+    c = synth.make_case(variant, dtype, B, cap, lens, paged=paged, seed=113)
+    err = max_err(to_f64(hip_run(to_gpu(c))), oracle_run(c))
+    assert err <= TOL[dtype], (variant, dtype, paged, err)
+
+
 @pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", ["sliding", "global"])
@@ -68,21 +85,50 @@ def test_single_position_is_exact(variant, dtype, paged):
             assert torch.equal(got[b, h], exp), (b, h)
 
 
+def slice_boundary_positions(variant, lens, cap):
+    """For each sequence, the first position of a tile that starts a new wave
+    slice inside kv head 0's unit (the position where two slices of the
+    stream partition meet), or the unit's middle if one slice holds it."""
+    KV = 16 if variant == "sliding" else 4
+    plan = gqa.gqa_decode_plan(variant, len(lens), cap)
+    W = plan["waves"] if plan["mode"] == "stream" else 1
+    rng = []
+    for L in lens:
+        L = min(L, cap)
+        lo = max(0, L - 1024) if variant == "sliding" else 0
+        t0 = lo // 16
+        rng.append((lo, L, t0, (L + 15) // 16 - t0))
+    T = KV * sum(n for *_, n in rng)
+    out, first = [], 0
+    for lo, L, t0, n in rng:
+        s0 = first                       # flattened first tile of unit (b, g=0)
+        pos = (lo + L) // 2
+        for w in range(W):
+            st = w * T // W
+            if s0 < st < s0 + n:
+                pos = max(lo, (t0 + st - s0) * 16)
+                break
+        out.append(min(pos, L - 1))
+        first += KV * n
+    return out
+
+
 @pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 def test_one_hot_dominant_logit_selects_exactly(variant, dtype, paged):
     lens = [1030, 200, 47, 1024, 1296]
     cap = 1296
-    n_split, tps = gqa.gqa_decode_plan(variant, len(lens), cap)
-    for pick in ("lo", "last", "page0", "page15", "split"):
-        pos = []
-        for L in lens:
-            lo = max(0, L - 1024) if variant == "sliding" else 0
-            first = ((lo + 15) // 16) * 16
-            p = {"lo": lo, "last": L - 1, "page0": first, "page15": first + 15,
-                 "split": (lo // 16 + tps) * 16}[pick]
-            pos.append(min(p, L - 1))
+    for pick in ("lo", "last", "page0", "page15", "slice"):
+        if pick == "slice":
+            pos = slice_boundary_positions(variant, lens, cap)
+        else:
+            pos = []
+            for L in lens:
+                lo = max(0, L - 1024) if variant == "sliding" else 0
+                first = ((lo + 15) // 16) * 16
+                p = {"lo": lo, "last": L - 1, "page0": first, "page15": first + 15}[pick]
+                pos.append(min(p, L - 1))
         c = oracle_pins.one_hot_case(variant, dtype, len(lens), cap, lens, pos, seed=103,
                                      paged=paged)
         got = hip_run(to_gpu(c)).cpu()
@@ -174,10 +220,9 @@ def test_profile_hooks_count_launches():
     for _ in range(3):
         hip_run(c)
     res = gqa.profile_read()
-    n_split, _ = gqa.gqa_decode_plan("global", 2, 4096)
-    assert res[("global", "split")][0] == 3 and res[("global", "split")][1] > 0
-    assert res[("global", "combine")][0] == (3 if n_split > 1 else 0)
-    assert res[("sliding", "split")][0] == 0
+    assert res[("global", "main")][0] == 3 and res[("global", "main")][1] > 0
+    assert res[("global", "combine")][0] == 3
+    assert res[("sliding", "main")][0] == 0
 
 
 def test_measurement_probes():
