@@ -104,7 +104,7 @@ def read_traffic():
     if vals.get("source_sha256") != source_hash():
         return None
     try:
-        return float(vals["global_split_hbm_bytes_per_launch"])
+        return float(vals["global_main_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
