@@ -32,6 +32,9 @@ METRIC = ("decode-attn K/V read GB/s and % of HBM peak; µs per call "
           "(sliding B=256, global B=32)")
 SLIDING = "sliding_bf16_b256_s8192"
 GLOBAL = "global_bf16_b32_paged_s16k_128k"
+# runtime windows of the sliding geometry measured beside the step (per-layer
+# windows of the Retrofit Plan page's progressive window table)
+SWEEP_WINDOWS = (2048, 4096, 8192)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sliding_b256_global_b32_paged.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd", "csrc",
                              "gqa_decode.hip")
@@ -171,13 +174,14 @@ def main():
     gqa.library()
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    log("generating the sliding B=256 contiguous cache")
-    sl = synth.make_workload(SLIDING, seed=args.seed, device=dev, fill=0.0)
+    log("generating the sliding B=256 contiguous cache (rows drawn for the widest window)")
+    sl = synth.make_workload(SLIDING, seed=args.seed, device=dev, fill=0.0,
+                             window=max(SWEEP_WINDOWS))
     log("generating the global B=32 paged cache")
     gl = synth.make_workload(GLOBAL, seed=args.seed, device=dev, fill=0.0)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
-    sl_bytes, gl_bytes = sl.kv_bytes(), gl.kv_bytes()
+    sl_bytes, gl_bytes = sl.kv_bytes(window=1024), gl.kv_bytes()
 
     o_sl = torch.empty_like(sl.q)
     o_gl = torch.empty_like(gl.q)
@@ -277,6 +281,30 @@ def main():
             "traffic": traffic,
         },
     }
+    log("window sweep of the sliding geometry")
+    sweep = []
+    for W in SWEEP_WINDOWS:
+        need = gqa.gqa_decode_workspace_bytes("sliding", sl.B, sl.cap, window=W)
+        ws_w = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            gqa.gqa_decode_sliding_window(sl.q, sl.k, sl.v, sl.seq_lens, W, o=o_sl,
+                                          workspace=ws_w, stream=stream)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a_ev.record(stream)
+        for _ in range(reps):
+            gqa.gqa_decode_sliding_window(sl.q, sl.k, sl.v, sl.seq_lens, W, o=o_sl,
+                                          workspace=ws_w, stream=stream)
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        ms = a_ev.elapsed_time(b_ev) / reps
+        nb = sl.kv_bytes(window=W)
+        sweep.append({"window": W, "plan": gqa.gqa_decode_plan("sliding", sl.B, sl.cap, window=W),
+                      "kv_bytes_per_call": nb, "us_per_call": round(ms * 1e3, 2),
+                      "kv_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        del ws_w
+    line["config"]["sliding_window_sweep"] = sweep
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
     line["roofline"]["measured_read_stream_GBps"] = probes["read_GBps"]

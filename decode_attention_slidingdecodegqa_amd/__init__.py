@@ -10,6 +10,8 @@ the library is missing or no GPU is present the calls raise.
     gqa_decode_global(q, k, v, seq_lens)                decodeGQA, contiguous cache
     gqa_decode_sliding_paged(q, k_pool, v_pool, block_table, seq_lens)
     gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens)
+    gqa_decode_sliding_window(q, k, v, seq_lens, window)    sliding geometry, runtime window
+    gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, window)
 
 Shapes (attn.core of the gemma-4-31B Model Spec page): q [B,32,D]; contiguous
 k/v [B,S_max,KV,D]; paged pools [num_pages,16,KV,D] with block_table
@@ -30,6 +32,8 @@ from ._lib import (  # noqa: F401
     gqa_decode_plan,
     gqa_decode_sliding,
     gqa_decode_sliding_paged,
+    gqa_decode_sliding_window,
+    gqa_decode_sliding_window_paged,
     gqa_decode_workspace_bytes,
     gqa_status_str,
     hbm_copy_probe,

@@ -18,7 +18,9 @@ EXPORTED_SYMBOLS = (
     "gqa_decode_sliding", "gqa_decode_global", "gqa_decode_sliding_paged",
     "gqa_decode_global_paged", "gqa_decode_workspace_bytes", "gqa_decode_plan",
     "gqa_decode_constants", "gqa_status_str", "gqa_profile_begin", "gqa_profile_read",
-    "gqa_hbm_read_probe", "gqa_hbm_copy_probe",
+    "gqa_hbm_read_probe", "gqa_hbm_copy_probe", "gqa_decode_sliding_window",
+    "gqa_decode_sliding_window_paged", "gqa_decode_sliding_window_workspace_bytes",
+    "gqa_decode_sliding_window_plan",
 )
 
 
@@ -47,6 +49,15 @@ def library():
                        ("gqa_decode_sliding_paged", paged), ("gqa_decode_global_paged", paged)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lib.gqa_decode_sliding_window.argtypes = [p, p, p, p, p, i32, i32, i32, i32, p, sz, p]
+    lib.gqa_decode_sliding_window.restype = ctypes.c_int
+    lib.gqa_decode_sliding_window_paged.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, i32, p,
+                                                    sz, p]
+    lib.gqa_decode_sliding_window_paged.restype = ctypes.c_int
+    lib.gqa_decode_sliding_window_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.gqa_decode_sliding_window_workspace_bytes.restype = sz
+    lib.gqa_decode_sliding_window_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
+    lib.gqa_decode_sliding_window_plan.restype = ctypes.c_int
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32]
     lib.gqa_decode_workspace_bytes.restype = sz
     lib.gqa_decode_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
@@ -83,18 +94,31 @@ def constants(variant) -> dict:
     return dict(zip(("heads", "kv_heads", "head_dim", "window", "page"), (x.value for x in vals)))
 
 
-def gqa_decode_workspace_bytes(variant, B: int, capacity: int) -> int:
+def gqa_decode_workspace_bytes(variant, B: int, capacity: int, window: int | None = None) -> int:
+    """Workspace bytes; `window` (sliding only) selects the windowed calls' size."""
+    if window is not None:
+        if _variant(variant) != GQA_SLIDING:
+            raise ValueError("a runtime window applies to the sliding variant only")
+        return int(library().gqa_decode_sliding_window_workspace_bytes(int(B), int(capacity),
+                                                                       int(window)))
     return int(library().gqa_decode_workspace_bytes(_variant(variant), int(B), int(capacity)))
 
 
 GQA_MODE_UNIT, GQA_MODE_STREAM = 0, 1
 
 
-def gqa_decode_plan(variant, B: int, capacity: int) -> dict:
+def gqa_decode_plan(variant, B: int, capacity: int, window: int | None = None) -> dict:
     """Launch plan: {'mode': 'unit'|'stream', 'waves': W, 'slots': workspace slots}."""
     mode, n, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    rc = library().gqa_decode_plan(_variant(variant), int(B), int(capacity), ctypes.byref(mode),
-                                   ctypes.byref(n), ctypes.byref(t))
+    if window is not None:
+        if _variant(variant) != GQA_SLIDING:
+            raise ValueError("a runtime window applies to the sliding variant only")
+        rc = library().gqa_decode_sliding_window_plan(int(B), int(capacity), int(window),
+                                                      ctypes.byref(mode), ctypes.byref(n),
+                                                      ctypes.byref(t))
+    else:
+        rc = library().gqa_decode_plan(_variant(variant), int(B), int(capacity),
+                                       ctypes.byref(mode), ctypes.byref(n), ctypes.byref(t))
     if rc:
         raise GqaError("gqa_decode_plan", rc)
     return {"mode": "unit" if mode.value == GQA_MODE_UNIT else "stream", "waves": n.value,
@@ -158,7 +182,7 @@ def _dev(t: torch.Tensor, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _prepare(variant, q, seq_lens, o, workspace, capacity):
+def _prepare(variant, q, seq_lens, o, workspace, capacity, window=None):
     B = q.shape[0]
     D = 256 if variant == GQA_SLIDING else 512
     if q.dim() != 3 or q.shape[1:] != (HEADS, D):
@@ -169,7 +193,7 @@ def _prepare(variant, q, seq_lens, o, workspace, capacity):
         o = torch.empty_like(q)
     elif o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
-    need = gqa_decode_workspace_bytes(variant, B, capacity)
+    need = gqa_decode_workspace_bytes(variant, B, capacity, window)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -182,7 +206,7 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _contiguous_call(name, variant, q, k, v, seq_lens, o, workspace, stream):
+def _contiguous_call(name, variant, q, k, v, seq_lens, o, workspace, stream, window=None):
     KV = 16 if variant == GQA_SLIDING else 4
     D = 256 if variant == GQA_SLIDING else 512
     if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != (KV, D) or v.shape != k.shape:
@@ -190,16 +214,18 @@ def _contiguous_call(name, variant, q, k, v, seq_lens, o, workspace, stream):
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     S_max = k.shape[1]
-    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, S_max)
+    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, S_max, window)
     fn = getattr(library(), name)
+    shape = (B, S_max) if window is None else (B, S_max, int(window))
     rc = fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
-            B, S_max, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+            *shape, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
     if rc:
         raise GqaError(name, rc)
     return o
 
 
-def _paged_call(name, variant, q, k_pool, v_pool, block_table, seq_lens, o, workspace, stream):
+def _paged_call(name, variant, q, k_pool, v_pool, block_table, seq_lens, o, workspace, stream,
+                window=None):
     KV = 16 if variant == GQA_SLIDING else 4
     D = 256 if variant == GQA_SLIDING else 512
     if k_pool.dim() != 4 or k_pool.shape[1:] != (PAGE, KV, D) or v_pool.shape != k_pool.shape:
@@ -211,11 +237,12 @@ def _paged_call(name, variant, q, k_pool, v_pool, block_table, seq_lens, o, work
         raise ValueError("block_table must be int32 [B,max_pages]")
     max_pages = block_table.shape[1]
     num_pages = k_pool.shape[0]
-    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, max_pages * PAGE)
+    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, max_pages * PAGE, window)
     fn = getattr(library(), name)
+    shape = (B, num_pages) if window is None else (B, num_pages, int(window))
     rc = fn(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
             _dev(block_table, "block_table"), max_pages, _dev(seq_lens, "seq_lens"), _dev(o, "o"),
-            B, num_pages, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+            *shape, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
     if rc:
         raise GqaError(name, rc)
     return o
@@ -245,3 +272,16 @@ def gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens, o=None, wo
     """decodeGQA on a paged cache k_pool, v_pool [num_pages,16,4,512]."""
     return _paged_call("gqa_decode_global_paged", GQA_GLOBAL, q, k_pool, v_pool, block_table,
                        seq_lens, o, workspace, stream)
+
+
+def gqa_decode_sliding_window(q, k, v, seq_lens, window, o=None, workspace=None, stream=None):
+    """slidingDecodeGQA geometry with a runtime window on a contiguous cache."""
+    return _contiguous_call("gqa_decode_sliding_window", GQA_SLIDING, q, k, v, seq_lens, o,
+                            workspace, stream, window=window)
+
+
+def gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, window, o=None,
+                                    workspace=None, stream=None):
+    """slidingDecodeGQA geometry with a runtime window on a paged cache."""
+    return _paged_call("gqa_decode_sliding_window_paged", GQA_SLIDING, q, k_pool, v_pool,
+                       block_table, seq_lens, o, workspace, stream, window=window)

@@ -832,13 +832,15 @@ struct Plan {
   size_t prefix, ml, acc, total;
 };
 
-int make_plan(int variant, int B, int cap, Plan* P) {
+// window: attended positions per sequence (0 = every position below L)
+int make_plan(int variant, int B, int cap, int window, Plan* P) {
   VariantInfo vi;
   if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
   if (B < 1 || B > kMaxBatch || cap < 1 || cap > kMaxSeq) return GQA_ERR_SHAPE;
+  if (window < 0 || window > kMaxSeq) return GQA_ERR_SHAPE;
   int tiles_max = (cap + kTile - 1) / kTile;
-  if (vi.window > 0) {
-    const int wt = (vi.window + kTile - 1) / kTile + 1;
+  if (window > 0) {
+    const int wt = (window + kTile - 1) / kTile + 1;
     tiles_max = tiles_max < wt ? tiles_max : wt;
   }
   const int units = B * vi.KV;
@@ -896,7 +898,9 @@ CombineFn pick_combine(bool bf16) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int run(int variant, bool paged, const void* q, const void* k, const void* v,
+inline int default_window(int variant) { return variant == GQA_SLIDING ? kSlidingWindow : 0; }
+
+int run(int variant, int window, bool paged, const void* q, const void* k, const void* v,
         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens, void* o,
         int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype, void* workspace,
         size_t workspace_bytes_given, void* stream_) {
@@ -915,7 +919,7 @@ int run(int variant, bool paged, const void* q, const void* k, const void* v,
   VariantInfo vi;
   variant_info(variant, &vi);
   Plan plan;
-  int rc = make_plan(variant, B, cap, &plan);
+  int rc = make_plan(variant, B, cap, window, &plan);
   if (rc) return rc;
   const bool unit_mode = plan.mode == GQA_MODE_UNIT;
   if (!unit_mode) {
@@ -940,7 +944,7 @@ int run(int variant, bool paged, const void* q, const void* k, const void* v,
   ka.cap = cap;
   ka.max_pages = paged ? max_pages : 0;
   ka.num_pages = paged ? num_pages : 0;
-  ka.window = vi.window;
+  ka.window = window;
   ka.n_waves = plan.waves;
 
   MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256>(unit_mode, paged, bf16)
@@ -976,14 +980,14 @@ extern "C" {
 int gqa_decode_sliding(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                        void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return run(GQA_SLIDING, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
+  return run(GQA_SLIDING, kSlidingWindow, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
              workspace_bytes, stream);
 }
 
 int gqa_decode_global(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                       void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return run(GQA_GLOBAL, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
+  return run(GQA_GLOBAL, 0, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
              workspace_bytes, stream);
 }
 
@@ -992,7 +996,7 @@ int gqa_decode_sliding_paged(const void* q, const void* k_pool, const void* v_po
                              const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
                              int32_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  return run(GQA_SLIDING, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
+  return run(GQA_SLIDING, kSlidingWindow, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
              num_pages, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -1001,20 +1005,57 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
                             const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
                             int32_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  return run(GQA_GLOBAL, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
+  return run(GQA_GLOBAL, 0, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
              num_pages, dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_sliding_window(const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, void* o, int32_t B, int32_t S_max,
+                              int32_t window, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (window < 1) return GQA_ERR_SHAPE;
+  return run(GQA_SLIDING, window, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype,
+             workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_sliding_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, void* o, int32_t B,
+                                    int32_t num_pages, int32_t window, int32_t dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 1) return GQA_ERR_SHAPE;
+  return run(GQA_SLIDING, window, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B,
+             0, num_pages, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t gqa_decode_sliding_window_workspace_bytes(int32_t B, int32_t capacity, int32_t window) {
+  Plan p;
+  if (window < 1 || make_plan(GQA_SLIDING, B, capacity, window, &p)) return 0;
+  return p.total;
+}
+
+int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, int32_t* mode,
+                                   int32_t* n_waves, int32_t* n_slots) {
+  if (window < 1) return GQA_ERR_SHAPE;
+  Plan p;
+  int rc = make_plan(GQA_SLIDING, B, capacity, window, &p);
+  if (rc) return rc;
+  if (mode) *mode = p.mode;
+  if (n_waves) *n_waves = p.waves;
+  if (n_slots) *n_slots = p.slots;
+  return GQA_OK;
 }
 
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity) {
   Plan p;
-  if (make_plan(variant, B, capacity, &p)) return 0;
+  if (make_plan(variant, B, capacity, default_window(variant), &p)) return 0;
   return p.total;
 }
 
 int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* mode,
                     int32_t* n_waves, int32_t* n_slots) {
   Plan p;
-  int rc = make_plan(variant, B, capacity, &p);
+  int rc = make_plan(variant, B, capacity, default_window(variant), &p);
   if (rc) return rc;
   if (mode) *mode = p.mode;
   if (n_waves) *n_waves = p.waves;

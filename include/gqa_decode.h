@@ -106,6 +106,30 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
                             int32_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* slidingDecodeGQA with a runtime window: the kv-head geometry of the sliding
+ * layers (32 query heads over 16 kv heads, D = 256, scale 1) attending to the
+ * last `window` positions below seq_lens[b], i.e. [max(0, L-window), L).
+ * This is the per-layer window of the Retrofit Plan page ("Progressive Window
+ * Assignment" table: 1024, 2048, 4096, 8192 in the four sliding layers of a
+ * block, each with its own full-length cache); any 1 <= window <= 262144 is
+ * accepted (GQA_ERR_SHAPE otherwise).  Arguments, layouts and errors are those
+ * of gqa_decode_sliding / gqa_decode_sliding_paged; the workspace size comes
+ * from gqa_decode_sliding_window_workspace_bytes. */
+int gqa_decode_sliding_window(const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, void* o, int32_t B, int32_t S_max,
+                              int32_t window, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int gqa_decode_sliding_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, void* o, int32_t B,
+                                    int32_t num_pages, int32_t window, int32_t dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes and launch plan of the windowed calls (0 / GQA_ERR_SHAPE for
+ * out-of-range arguments); see gqa_decode_workspace_bytes and gqa_decode_plan. */
+size_t gqa_decode_sliding_window_workspace_bytes(int32_t B, int32_t capacity, int32_t window);
+int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, int32_t* mode,
+                                   int32_t* n_waves, int32_t* n_slots);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:

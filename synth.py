@@ -81,17 +81,23 @@ class Case:
     def D(self):
         return VARIANTS[self.variant][1]
 
-    def attended(self, b: int) -> tuple[int, int]:
-        """[lo, L) of sequence b (the range the variant attends to)."""
+    def attended(self, b: int, window: int | None = None) -> tuple[int, int]:
+        """[lo, L) of sequence b under `window` (default: the case's window; 0 = none)."""
+        W = self.window if window is None else window
         L = int(self.seq_lens[b])
         L = max(0, min(L, self.cap))
-        lo = max(0, L - self.window) if self.window > 0 else 0
+        lo = max(0, L - W) if W > 0 else 0
         return lo, L
 
-    def kv_bytes(self) -> int:
+    def kv_bytes(self, window: int | None = None) -> int:
         """Algorithmic K+V bytes one call reads (each attended row once)."""
         eb = 4 if self.dtype == "f32" else 2
-        n = sum(L - lo for lo, L in (self.attended(b) for b in range(self.B)))
+        lens = self.seq_lens.tolist()
+        W = self.window if window is None else window
+        n = 0
+        for L in lens:
+            L = max(0, min(int(L), self.cap))
+            n += L - (max(0, L - W) if W > 0 else 0)
         return n * self.KV * self.D * 2 * eb
 
 
@@ -212,13 +218,14 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
 
 
 def make_workload(name: str, seed: int = 0, device="cpu", fill: float = float("nan"),
-                  B: int | None = None) -> Case:
-    """One of WORKLOADS by name (B may be cut down for a quick CPU-sized run)."""
+                  B: int | None = None, window: int | None = None) -> Case:
+    """One of WORKLOADS by name (B may be cut down for a quick CPU-sized run; `window`
+    overrides the variant's window, which decides the rows drawn)."""
     w = WORKLOADS[name]
     nb = w["B"] if B is None else B
     lens = draw_seq_lens(w["lens"], w["B"], seed)[:nb]
     return make_case(w["variant"], w["dtype"], nb, w["cap"], lens, paged=w["paged"], seed=seed,
-                     device=device, fill=fill)
+                     device=device, fill=fill, window=window)
 
 
 def to_numpy(t: torch.Tensor):

@@ -12,7 +12,14 @@ import synth
 TOL = {"f32": 1e-4, "bf16": 2e-2}  # max-abs error bars for unit-RMS values
 
 
-def hip_run(case: synth.Case, workspace=None, stream=None, o=None) -> torch.Tensor:
+def hip_run(case: synth.Case, workspace=None, stream=None, o=None, window=None) -> torch.Tensor:
+    if window is not None:
+        if case.block_table is None:
+            return gqa.gqa_decode_sliding_window(case.q, case.k, case.v, case.seq_lens, window,
+                                                 o=o, workspace=workspace, stream=stream)
+        return gqa.gqa_decode_sliding_window_paged(case.q, case.k, case.v, case.block_table,
+                                                   case.seq_lens, window, o=o,
+                                                   workspace=workspace, stream=stream)
     if case.variant == "sliding":
         fn_c, fn_p = gqa.gqa_decode_sliding, gqa.gqa_decode_sliding_paged
     else:

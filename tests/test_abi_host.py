@@ -132,6 +132,25 @@ def test_bad_arguments_fail_before_launch(lib):
     assert gqa.gqa_status_str(-99) == "unknown status"
 
 
+def test_window_arguments(lib):
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    f = lib.gqa_decode_sliding_window
+    fp = lib.gqa_decode_sliding_window_paged
+    for w in (0, -1, 262145):
+        assert f(ok, ok, ok, ok, ok, 4, 2048, w, 1, None, 0, None) == -2
+        assert fp(ok, ok, ok, ok, 16, ok, ok, 4, 16, w, 1, None, 0, None) == -2
+        assert lib.gqa_decode_sliding_window_workspace_bytes(4, 2048, w) == 0
+    # the default window reproduces the sliding plan; larger windows leave unit mode
+    assert gqa.gqa_decode_plan("sliding", 256, 8192, window=1024) == \
+        gqa.gqa_decode_plan("sliding", 256, 8192)
+    assert gqa.gqa_decode_plan("sliding", 256, 8192, window=8192)["mode"] == "stream"
+    assert gqa.gqa_decode_plan("sliding", 256, 8192, window=2032)["mode"] == "unit"
+    assert gqa.gqa_decode_workspace_bytes("sliding", 256, 8192, window=8192) > 0
+    with pytest.raises(ValueError):
+        gqa.gqa_decode_plan("global", 4, 4096, window=1024)
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     q = torch.zeros(1, 32, 256, dtype=torch.bfloat16)

@@ -241,6 +241,69 @@ def test_measurement_probes():
     assert torch.equal(s2, d2)
 
 
+# --------------------------------------------------------------- runtime window
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("window", [1, 17, 512, 2048, 4096, 8192])
+def test_window_parity(window, paged):
+    cap = 9008
+    lens = [1, window, window + 1, 4000, 9008, 8191]
+    c = synth.make_case("sliding", "bf16", len(lens), cap, lens, paged=paged, seed=120,
+                        window=window, extra_pages=3)
+    got = to_f64(hip_run(to_gpu(c), window=window))
+    err = max_err(got, oracle_run(c, window=window))
+    assert err <= TOL["bf16"], (window, paged, err)
+
+
+@pytest.mark.parametrize("window", [512, 2048])
+def test_window_parity_unit_mode_and_f32(window):
+    B, cap = 64, 4096
+    mode = gqa.gqa_decode_plan("sliding", B, cap, window=window)["mode"]
+    assert mode == ("unit" if window == 512 else "stream")
+    lens = synth.draw_seq_lens(("uniform", 1, cap), B, 9)
+    c = synth.make_case("sliding", "f32", B, cap, lens, seed=121, window=window)
+    err = max_err(to_f64(hip_run(to_gpu(c), window=window)), oracle_run(c, window=window))
+    assert err <= TOL["f32"], (window, err)
+
+
+def test_window_1024_matches_the_default_entry_point():
+    c = to_gpu(synth.make_case("sliding", "bf16", 5, 3000, [3000, 1025, 1024, 5, 2500], seed=122))
+    assert torch.equal(hip_run(c), hip_run(c, window=1024))
+
+
+@pytest.mark.parametrize("window", [2048, 8192])
+def test_window_one_hot_edges_exact(window):
+    lens = [window + 37, window, 9000]
+    cap = 9008
+    for pick in ("lo", "last"):
+        pos = [max(0, L - window) if pick == "lo" else L - 1 for L in lens]
+        c = synth.make_case("sliding", "f32", 3, cap, lens, seed=123, window=window)
+        G = 2
+        js = [(h * 37 + 5) % 256 for h in range(HEADS)]
+        q = torch.zeros(3, HEADS, 256)
+        for h in range(HEADS):
+            q[:, h, js[h]] = 1.0
+        c.q = q
+        for b in range(3):
+            lo, L = c.attended(b)
+            for h in range(HEADS):
+                c.k[b, lo:L, h // G, js[h]] = torch.linspace(-4, 4, L - lo)
+                c.k[b, pos[b], h // G, js[h]] = 160.0
+        got = hip_run(to_gpu(c), window=window).cpu()
+        for b in range(3):
+            for h in range(HEADS):
+                assert torch.equal(got[b, h], c.v[b, pos[b], h // G]), (pick, b, h)
+
+
+def test_window_poison_never_read():
+    lens = [5000, 20, 9000]
+    kw = dict(paged=True, seed=124, window=4096, extra_pages=4)
+    a = synth.make_case("sliding", "bf16", 3, 9008, lens, fill=float("nan"), **kw)
+    z = synth.make_case("sliding", "bf16", 3, 9008, lens, fill=0.0, **kw)
+    ga, gz = hip_run(to_gpu(a), window=4096).cpu(), hip_run(to_gpu(z), window=4096).cpu()
+    assert torch.isfinite(ga.float()).all() and torch.equal(ga, gz)
+
+
 # --------------------------------------------------------------- full-size workloads
 
 def _sample_rows(case, n_seq, seed):
