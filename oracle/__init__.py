@@ -67,6 +67,9 @@ def load(path: str = LIBRARY):
     fn.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, i32,
                    p, i32]
     fn.restype = ctypes.c_int
+    ap = lib.oracle_gqa_append_rows
+    ap.argtypes = [ctypes.c_int, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
+    ap.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -134,3 +137,38 @@ def gqa_decode(variant, q, k, v, seq_lens, block_table=None, num_pages=None, row
     if rc != 0:
         raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
     return out.reshape(B, HEADS, D) if rows is None else out
+
+
+def gqa_append_rows(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, lib=None):
+    """Norms + RoPE of the new token of every sequence (attn.qk_norm, attn.v_norm,
+    attn.rope of the Model Spec page), in fp64.
+
+    q_raw [B,32,D], k_raw/v_raw [B,KV,D] (v_raw ignored for "global": values =
+    keys), w_q/w_k [D]; float32 arrays or uint16 bf16 bits.  Returns
+    (q_out [B,32,D], k_row [B,KV,D], v_row [B,KV,D], pos [B]) with pos =
+    seq_lens - 1 (-1 and zero rows where seq_lens < 1).
+    """
+    KV, D, _ = VARIANTS[variant]
+    lib = lib or load()
+    q_raw, k_raw = np.ascontiguousarray(q_raw), np.ascontiguousarray(k_raw)
+    w_q, w_k = np.ascontiguousarray(w_q), np.ascontiguousarray(w_k)
+    dt = _dtype_code(q_raw)
+    v_raw = None if v_raw is None else np.ascontiguousarray(v_raw)
+    for a in (k_raw, w_q, w_k) + ((v_raw,) if v_raw is not None else ()):
+        if _dtype_code(a) != dt:
+            raise TypeError("inputs must share a dtype")
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = q_raw.shape[0]
+    if q_raw.shape != (B, HEADS, D) or k_raw.shape != (B, KV, D) or w_q.shape != (D,) or \
+            w_k.shape != (D,) or seq_lens.shape != (B,):
+        raise ValueError("bad shapes")
+    q_out = np.zeros((B, HEADS, D))
+    k_row = np.zeros((B, KV, D))
+    v_row = np.zeros((B, KV, D))
+    pos = np.zeros(B, dtype=np.int32)
+    rc = lib.oracle_gqa_append_rows(dt, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(w_q),
+                                    _ptr(w_k), _ptr(seq_lens), B, KV, D, _ptr(q_out),
+                                    _ptr(k_row), _ptr(v_row), _ptr(pos))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
+    return q_out, k_row, v_row, pos

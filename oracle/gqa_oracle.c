@@ -208,3 +208,100 @@ int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
   pthread_mutex_destroy(&j.mu);
   return j.err;
 }
+
+/*
+ * ---- KV append with the per-head norms and RoPE of the new token ----------
+ *
+ * The nodes between the projections and attn.core on the gemma-4-31B Model
+ * Spec page ("Compute-graph nodes" table), applied to one new token per
+ * sequence whose position is pos = seq_lens[b] - 1 (the cache already counts
+ * it, as the architecture page's compact forward pass appends before
+ * attending):
+ *   attn.qk_norm  per head: y_i = x_i / sqrt(sum_j x_j^2 / D + eps) * w_i
+ *                 (one weight vector of length D for q, one for k)
+ *   attn.v_norm   per head: y_i = x_i / sqrt(sum_j x_j^2 / D + eps)
+ *   attn.rope     rotate pairs (i, i + D/2) by pos * theta^(-2i/D) for
+ *                 i < active, other coordinates unchanged:
+ *                 (a, b) -> (a cos - b sin, a sin + b cos)
+ *                 sliding: D = 256, theta = 1e4, active = 128
+ *                 global:  D = 512, theta = 1e6, active = 64
+ *   values = keys on global layers: v_raw is k_raw.
+ * Outputs (double): q_out [B,32,D] = rope(qk_norm(q_raw, w_q)),
+ * k_row [B,KV,D] = rope(qk_norm(k_raw, w_k)), v_row [B,KV,D] = v_norm(v_raw);
+ * pos_out[b] = seq_lens[b] - 1.  Sequences with seq_lens[b] < 1 get zero rows
+ * and pos_out = -1 (nothing to append).
+ */
+
+#define ORC_EPS 1e-6
+
+static void orc_rms(const double* x, int D, const double* w, double* y) {
+  double ss = 0.0;
+  for (int d = 0; d < D; ++d) ss += x[d] * x[d];
+  const double inv = 1.0 / sqrt(ss / D + ORC_EPS);
+  for (int d = 0; d < D; ++d) y[d] = x[d] * inv * (w ? w[d] : 1.0);
+}
+
+static void orc_rope(double* y, int D, long pos, double theta, int active) {
+  const int h = D / 2;
+  for (int i = 0; i < active; ++i) {
+    const double ang = (double)pos * pow(theta, -2.0 * i / D);
+    const double c = cos(ang), s = sin(ang);
+    const double a = y[i], b = y[i + h];
+    y[i] = a * c - b * s;
+    y[i + h] = a * s + b * c;
+  }
+}
+
+/*
+ * oracle_gqa_append_rows
+ *   dtype      ORC_F32 or ORC_BF16 for q_raw, k_raw, v_raw, w_q, w_k
+ *   q_raw      [B, 32, D];  k_raw, v_raw [B, KV, D] (v_raw unused when KV = 4)
+ *   w_q, w_k   [D]
+ *   KV, D      16/256 (sliding) or 4/512 (global)
+ * Returns 0 or ORC_ERR_ARG.
+ */
+int oracle_gqa_append_rows(int dtype, const void* q_raw, const void* k_raw, const void* v_raw,
+                           const void* w_q, const void* w_k, const int32_t* seq_lens, int32_t B,
+                           int32_t KV, int32_t D, double* q_out, double* k_row, double* v_row,
+                           int32_t* pos_out) {
+  if (!q_raw || !k_raw || !w_q || !w_k || !seq_lens || !q_out || !k_row || !v_row || !pos_out)
+    return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
+  const int global = KV == 4;
+  if (!(KV == 16 && D == 256) && !(KV == 4 && D == 512)) return ORC_ERR_ARG;
+  if (!global && !v_raw) return ORC_ERR_ARG;
+  const double theta = global ? 1e6 : 1e4;
+  const int active = global ? 64 : 128;
+  double* wq = (double*)malloc(sizeof(double) * D);
+  double* wk = (double*)malloc(sizeof(double) * D);
+  double* x = (double*)malloc(sizeof(double) * D);
+  if (!wq || !wk || !x) { free(wq); free(wk); free(x); return ORC_ERR_NOMEM; }
+  for (int d = 0; d < D; ++d) {
+    wq[d] = orc_elem(w_q, dtype, d);
+    wk[d] = orc_elem(w_k, dtype, d);
+  }
+  for (int b = 0; b < B; ++b) {
+    const long pos = (long)seq_lens[b] - 1;
+    pos_out[b] = pos >= 0 ? (int32_t)pos : -1;
+    for (int h = 0; h < ORC_HEADS; ++h) {
+      double* y = q_out + ((size_t)b * ORC_HEADS + h) * D;
+      if (pos < 0) { for (int d = 0; d < D; ++d) y[d] = 0.0; continue; }
+      for (int d = 0; d < D; ++d) x[d] = orc_elem(q_raw, dtype, ((size_t)b * ORC_HEADS + h) * D + d);
+      orc_rms(x, D, wq, y);
+      orc_rope(y, D, pos, theta, active);
+    }
+    for (int g = 0; g < KV; ++g) {
+      double* yk = k_row + ((size_t)b * KV + g) * D;
+      double* yv = v_row + ((size_t)b * KV + g) * D;
+      if (pos < 0) { for (int d = 0; d < D; ++d) yk[d] = yv[d] = 0.0; continue; }
+      for (int d = 0; d < D; ++d) x[d] = orc_elem(k_raw, dtype, ((size_t)b * KV + g) * D + d);
+      orc_rms(x, D, wk, yk);
+      orc_rope(yk, D, pos, theta, active);
+      if (!global)
+        for (int d = 0; d < D; ++d) x[d] = orc_elem(v_raw, dtype, ((size_t)b * KV + g) * D + d);
+      orc_rms(x, D, NULL, yv);  /* global: values are the raw keys, unit-normalised */
+    }
+  }
+  free(wq); free(wk); free(x);
+  return ORC_OK;
+}
