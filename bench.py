@@ -305,6 +305,39 @@ def main():
                       "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         del ws_w
     line["config"]["sliding_window_sweep"] = sweep
+    log("KV append (norms + RoPE of the new token, cache write)")
+    app = {}
+    gen = torch.Generator(device=dev).manual_seed(args.seed + 7)
+    for name, case in (("sliding_b256_contiguous", sl), ("global_b32_paged", gl)):
+        KV, D = case.KV, case.D
+        tok = [torch.randn(case.B, n, D, device=dev, generator=gen).to(torch.bfloat16)
+               for n in (32, KV, KV)]
+        wq, wk = (torch.empty(D, device=dev).uniform_(0.2, 0.4, generator=gen)
+                  .to(torch.bfloat16) for _ in range(2))
+        q_out = torch.empty_like(tok[0])
+        if case.variant == "sliding":
+            call = lambda: gqa.gqa_append_sliding(tok[0], tok[1], tok[2], wq, wk, case.seq_lens,
+                                                  case.k, case.v, block_table=case.block_table,
+                                                  q_out=q_out, stream=stream)
+        else:
+            call = lambda: gqa.gqa_append_global(tok[0], tok[1], wq, wk, case.seq_lens, case.k,
+                                                 case.v, block_table=case.block_table,
+                                                 q_out=q_out, stream=stream)
+        for _ in range(3):
+            call()
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        a_ev.record(stream)
+        for _ in range(reps):
+            call()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        ms = a_ev.elapsed_time(b_ev) / reps
+        rows_in = 32 + KV * (2 if case.variant == "sliding" else 1)
+        moved = case.B * (rows_in + 32 + 2 * KV) * D * 2 + 2 * D * 2
+        app[name] = {"B": case.B, "us_per_call": round(ms * 1e3, 2), "bytes_per_call": moved,
+                     "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    line["config"]["append"] = app
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
     line["roofline"]["measured_read_stream_GBps"] = probes["read_GBps"]

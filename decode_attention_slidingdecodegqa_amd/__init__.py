@@ -12,6 +12,9 @@ the library is missing or no GPU is present the calls raise.
     gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens)
     gqa_decode_sliding_window(q, k, v, seq_lens, window)    sliding geometry, runtime window
     gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, window)
+    gqa_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
+    gqa_append_global(q_raw, k_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
+                                                        new token: norms, RoPE, cache write
 
 Shapes (attn.core of the gemma-4-31B Model Spec page): q [B,32,D]; contiguous
 k/v [B,S_max,KV,D]; paged pools [num_pages,16,KV,D] with block_table
@@ -27,6 +30,8 @@ from ._lib import (  # noqa: F401
     GQA_SLIDING,
     GqaError,
     constants,
+    gqa_append_global,
+    gqa_append_sliding,
     gqa_decode_global,
     gqa_decode_global_paged,
     gqa_decode_plan,

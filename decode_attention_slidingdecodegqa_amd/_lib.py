@@ -20,7 +20,8 @@ EXPORTED_SYMBOLS = (
     "gqa_decode_constants", "gqa_status_str", "gqa_profile_begin", "gqa_profile_read",
     "gqa_hbm_read_probe", "gqa_hbm_copy_probe", "gqa_decode_sliding_window",
     "gqa_decode_sliding_window_paged", "gqa_decode_sliding_window_workspace_bytes",
-    "gqa_decode_sliding_window_plan",
+    "gqa_decode_sliding_window_plan", "gqa_append_sliding", "gqa_append_sliding_paged",
+    "gqa_append_global", "gqa_append_global_paged",
 )
 
 
@@ -58,6 +59,13 @@ def library():
     lib.gqa_decode_sliding_window_workspace_bytes.restype = sz
     lib.gqa_decode_sliding_window_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
     lib.gqa_decode_sliding_window_plan.restype = ctypes.c_int
+    lib.gqa_append_sliding.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_append_sliding_paged.argtypes = [p, p, p, p, p, p, i32, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_append_global.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_append_global_paged.argtypes = [p, p, p, p, p, i32, p, p, p, p, i32, i32, i32, p]
+    for name in ("gqa_append_sliding", "gqa_append_sliding_paged", "gqa_append_global",
+                 "gqa_append_global_paged"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32]
     lib.gqa_decode_workspace_bytes.restype = sz
     lib.gqa_decode_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
@@ -133,16 +141,16 @@ def profile_begin(capacity: int) -> None:
 
 def profile_read() -> dict:
     """{(variant, kernel): (launches, total_ms)} for variant in sliding/global and
-    kernel in main/combine (the stream kernel and the split combine)."""
-    counts = (ctypes.c_int32 * 4)()
-    ms = (ctypes.c_double * 4)()
-    rc = library().gqa_profile_read(counts, ms, 4)
+    kernel in main/combine/append."""
+    counts = (ctypes.c_int32 * 6)()
+    ms = (ctypes.c_double * 6)()
+    rc = library().gqa_profile_read(counts, ms, 6)
     if rc:
         raise GqaError("gqa_profile_read", rc)
     out = {}
     for vi, vname in enumerate(("sliding", "global")):
-        for ki, kname in enumerate(("main", "combine")):
-            out[(vname, kname)] = (counts[2 * vi + ki], ms[2 * vi + ki])
+        for kind, kname in ((2 * vi, "main"), (2 * vi + 1, "combine"), (4 + vi, "append")):
+            out[(vname, kname)] = (counts[kind], ms[kind])
     return out
 
 
@@ -285,3 +293,72 @@ def gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, wi
     """slidingDecodeGQA geometry with a runtime window on a paged cache."""
     return _paged_call("gqa_decode_sliding_window_paged", GQA_SLIDING, q, k_pool, v_pool,
                        block_table, seq_lens, o, workspace, stream, window=window)
+
+
+def _append_call(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
+                 block_table, q_out, stream):
+    KV = 16 if variant == GQA_SLIDING else 4
+    D = 256 if variant == GQA_SLIDING else 512
+    B = q_raw.shape[0]
+    if q_raw.shape != (B, HEADS, D) or k_raw.shape != (B, KV, D):
+        raise ValueError(f"q_raw must be [B,32,{D}] and k_raw [B,{KV},{D}]")
+    if variant == GQA_SLIDING and (v_raw is None or v_raw.shape != k_raw.shape):
+        raise ValueError("v_raw must be [B,16,256]")
+    if w_q.shape != (D,) or w_k.shape != (D,):
+        raise ValueError(f"w_q and w_k must be [{D}]")
+    dts = {t.dtype for t in (q_raw, k_raw, w_q, w_k, k_cache, v_cache)
+           if t is not None}
+    if v_raw is not None and variant == GQA_SLIDING:
+        dts.add(v_raw.dtype)
+    if len(dts) != 1:
+        raise TypeError("inputs, weights and caches must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if q_out is None:
+        q_out = torch.empty_like(q_raw)
+    lib = library()
+    st = _stream(stream, q_raw.device)
+    ptrs = [_dev(q_raw, "q_raw"), _dev(k_raw, "k_raw")]
+    if variant == GQA_SLIDING:
+        ptrs.append(_dev(v_raw, "v_raw"))
+    ptrs += [_dev(w_q, "w_q"), _dev(w_k, "w_k")]
+    dt = _dtype_code(q_raw)
+    name = "gqa_append_" + ("sliding" if variant == GQA_SLIDING else "global")
+    if block_table is None:
+        if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[2:] != (KV, D) or \
+                v_cache.shape != k_cache.shape:
+            raise ValueError(f"k_cache/v_cache must be [B,S_max,{KV},{D}]")
+        rc = getattr(lib, name)(*ptrs, _dev(seq_lens, "seq_lens"), _dev(q_out, "q_out"),
+                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B,
+                                k_cache.shape[1], dt, st)
+    else:
+        name += "_paged"
+        if k_cache.dim() != 4 or k_cache.shape[1:] != (PAGE, KV, D) or \
+                v_cache.shape != k_cache.shape:
+            raise ValueError(f"k_pool/v_pool must be [num_pages,16,{KV},{D}]")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B,max_pages]")
+        rc = getattr(lib, name)(*ptrs, _dev(block_table, "block_table"), block_table.shape[1],
+                                _dev(seq_lens, "seq_lens"), _dev(q_out, "q_out"),
+                                _dev(k_cache, "k_pool"), _dev(v_cache, "v_pool"), B,
+                                k_cache.shape[0], dt, st)
+    if rc:
+        raise GqaError(name, rc)
+    return q_out
+
+
+def gqa_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
+                       block_table=None, q_out=None, stream=None):
+    """Norms + RoPE of the new token (position seq_lens-1) of the sliding layers;
+    writes q_out (returned) and the token's K/V rows into the cache (contiguous,
+    or paged when block_table is given)."""
+    return _append_call(GQA_SLIDING, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
+                        block_table, q_out, stream)
+
+
+def gqa_append_global(q_raw, k_raw, w_q, w_k, seq_lens, k_cache, v_cache, block_table=None,
+                      q_out=None, stream=None):
+    """As gqa_append_sliding for the global layers (values = keys: no v_raw)."""
+    return _append_call(GQA_GLOBAL, q_raw, k_raw, None, w_q, w_k, seq_lens, k_cache, v_cache,
+                        block_table, q_out, stream)

@@ -749,6 +749,173 @@ __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
   }
 }
 
+// ------------------------------------------------------------- KV append
+// The nodes between the projections and attn.core (Model Spec page,
+// "Compute-graph nodes" table) for the new token of each sequence, at
+// position pos = seq_lens[b] - 1:
+//   q_out = rope(qk_norm(q_raw, w_q)), k_row = rope(qk_norm(k_raw, w_k)),
+//   v_row = v_norm(v_raw) (global layers: values = keys, v_raw = k_raw);
+//   qk_norm / v_norm: x / sqrt(mean(x^2) + 1e-6) (* w);
+//   rope: rotate pairs (i, i + D/2) by pos * theta^(-2i/D) for i < active
+//   (sliding theta 1e4, all 128 pairs; global theta 1e6, the first 64 pairs).
+// k_row and v_row are written into the cache at pos.  Work-group (b, y) takes
+// head rows 4y .. 4y+3 of sequence b (q heads, then k heads, then v heads),
+// one row per wave, lane l holding elements [l*D/64, (l+1)*D/64), so the RoPE
+// partner of a first-half element sits in lane l + 32; the group's cos/sin
+// table is formed in double precision (angles reach 2.6e5 radians) in LDS.
+
+struct AppendArgs {
+  const char* q_raw;
+  const char* k_raw;
+  const char* v_raw;  // unused on global layers (values = keys)
+  const char* w_q;
+  const char* w_k;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  char* q_out;
+  char* k_cache;
+  char* v_cache;
+  int32_t B;
+  int32_t cap;
+  int32_t max_pages;
+  int32_t num_pages;
+};
+
+template <int N, bool BF16>
+__device__ inline void load_elems(const char* p, float (&x)[N]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(p + 8 * c);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const unsigned d = w[q];
+        x[4 * c + 2 * q] = bf16_value(d & 0xffffu);
+        x[4 * c + 2 * q + 1] = bf16_value(d >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p + 16 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[4 * c + q] = w[q];
+    }
+  }
+}
+
+template <int N, bool BF16>
+__device__ inline void store_elems(char* p, const float (&x)[N]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c)
+      *reinterpret_cast<u32x2*>(p + 8 * c) =
+          u32x2{bf16_bits(x[4 * c]) | (bf16_bits(x[4 * c + 1]) << 16),
+                bf16_bits(x[4 * c + 2]) | (bf16_bits(x[4 * c + 3]) << 16)};
+  } else {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c)
+      *reinterpret_cast<f32x4*>(p + 16 * c) = f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
+  }
+}
+
+template <int KV, int D, bool PAGED, bool BF16>
+__global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
+  constexpr bool GLOBAL = KV == 4;
+  constexpr int H = D / 2;
+  constexpr int N = D / 64;  // elements per lane
+  constexpr int EB = Elem<BF16>::bytes;
+  constexpr int ROW = D * EB;
+  constexpr int ACTIVE = GLOBAL ? 64 : 128;
+  constexpr double LOG2_THETA = GLOBAL ? 19.931568569324174 : 13.287712379549449;  // log2 1e6, 1e4
+  constexpr int ROWS = kHeads + 2 * KV;  // q heads, then k heads, then v heads
+  __shared__ float s_cos[H];
+  __shared__ float s_sin[H];
+
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int L = a.seq_lens[b];
+  const bool live = L >= 1 && L <= a.cap;
+  const int row = blockIdx.y * kWaves + wave;
+  const int pos = L - 1;
+
+  // destination of the new token's cache rows
+  size_t row_off = 0;
+  bool write_cache = live;
+  if (live) {
+    if constexpr (PAGED) {
+      const int page = a.block_table[(size_t)b * a.max_pages + pos / kPage];
+      write_cache = page >= 0 && page < a.num_pages;
+      row_off = ((size_t)(write_cache ? page : 0) * kPage + pos % kPage) * KV * (size_t)ROW;
+    } else {
+      row_off = ((size_t)b * a.cap + pos) * KV * (size_t)ROW;
+    }
+  }
+
+  for (int i = threadIdx.x; i < H; i += kThreads) {
+    float c = 1.f, sn = 0.f;
+    if (live && i < ACTIVE) {
+      // theta^(-2i/D) and the angle in double, reduced to [-pi, pi] in double,
+      // then an fp32 sin/cos of the reduced angle
+      const double ang = (double)pos * exp2(-2.0 * i / D * LOG2_THETA);
+      const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+      sincosf((float)red, &sn, &c);
+    }
+    s_cos[i] = c;
+    s_sin[i] = sn;
+  }
+  __syncthreads();
+
+  float wq[N], wk[N];
+  load_elems<N, BF16>(a.w_q + (size_t)lane * N * EB, wq);
+  load_elems<N, BF16>(a.w_k + (size_t)lane * N * EB, wk);
+
+  if (row < ROWS) {
+    const bool is_q = row < kHeads;
+    const bool is_k = !is_q && row < kHeads + KV;
+    const int head = is_q ? row : (is_k ? row - kHeads : row - kHeads - KV);
+    char* dst;
+    const char* src;
+    if (is_q) {
+      src = a.q_raw + ((size_t)b * kHeads + head) * ROW;
+      dst = a.q_out + ((size_t)b * kHeads + head) * ROW;
+    } else {
+      src = ((is_k || GLOBAL) ? a.k_raw : a.v_raw) + ((size_t)b * KV + head) * ROW;
+      dst = (is_k ? a.k_cache : a.v_cache) + row_off + (size_t)head * ROW;
+    }
+    float y[N];
+    if (!live) {
+      // nothing to append: zero q rows, no cache write
+#pragma unroll
+      for (int e = 0; e < N; ++e) y[e] = 0.f;
+      if (is_q) store_elems<N, BF16>(dst + (size_t)lane * N * EB, y);
+      return;
+    }
+    float x[N];
+    load_elems<N, BF16>(src + (size_t)lane * N * EB, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float inv = 1.f / sqrtf(ss / D + 1e-6f);
+#pragma unroll
+    for (int e = 0; e < N; ++e) y[e] = x[e] * inv * (is_q ? wq[e] : (is_k ? wk[e] : 1.f));
+    if (is_q || is_k) {
+      const bool first = lane < 32;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float partner = __shfl_xor(y[e], 32);
+        const int i = (lane & 31) * N + e;  // pair index
+        const float c = s_cos[i], sn = s_sin[i];
+        y[e] = first ? y[e] * c - partner * sn : y[e] * c + partner * sn;
+      }
+    }
+    if (is_q || write_cache) store_elems<N, BF16>(dst + (size_t)lane * N * EB, y);
+  }
+}
+
 // ------------------------------------------------------- measurement kernels
 // Not part of the attention path: a plain read stream and a plain copy of a
 // known byte count, used to measure the sustainable HBM read rate of the part
@@ -973,6 +1140,65 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   return GQA_OK;
 }
 
+typedef void (*AppendFn)(AppendArgs);
+
+template <int KV, int D>
+AppendFn pick_append(bool paged, bool bf16) {
+  if (paged)
+    return bf16 ? gqa_append_kernel<KV, D, true, true> : gqa_append_kernel<KV, D, true, false>;
+  return bf16 ? gqa_append_kernel<KV, D, false, true> : gqa_append_kernel<KV, D, false, false>;
+}
+
+int run_append(int variant, bool paged, const void* q_raw, const void* k_raw, const void* v_raw,
+               const void* w_q, const void* w_k, const int32_t* block_table, int32_t max_pages,
+               const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache, int32_t B,
+               int32_t S_max, int32_t num_pages, int32_t dtype, void* stream_) {
+  const bool global = variant == GQA_GLOBAL;
+  if (!q_raw || !k_raw || (!global && !v_raw) || !w_q || !w_k || !seq_lens || !q_out ||
+      !k_cache || !v_cache || (paged && !block_table))
+    return GQA_ERR_NULL;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
+  if (B < 1 || B > kMaxBatch) return GQA_ERR_SHAPE;
+  int cap;
+  if (paged) {
+    if (max_pages < 1 || max_pages > kMaxSeq / kPage || num_pages < 1) return GQA_ERR_SHAPE;
+    cap = max_pages * kPage;
+  } else {
+    if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
+    cap = S_max;
+  }
+  if (!aligned16(q_raw) || !aligned16(k_raw) || (!global && !aligned16(v_raw)) ||
+      !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return GQA_ERR_ALIGN;
+  AppendArgs aa;
+  aa.q_raw = static_cast<const char*>(q_raw);
+  aa.k_raw = static_cast<const char*>(k_raw);
+  aa.v_raw = static_cast<const char*>(v_raw);
+  aa.w_q = static_cast<const char*>(w_q);
+  aa.w_k = static_cast<const char*>(w_k);
+  aa.seq_lens = seq_lens;
+  aa.block_table = block_table;
+  aa.q_out = static_cast<char*>(q_out);
+  aa.k_cache = static_cast<char*>(k_cache);
+  aa.v_cache = static_cast<char*>(v_cache);
+  aa.B = B;
+  aa.cap = cap;
+  aa.max_pages = paged ? max_pages : 0;
+  aa.num_pages = paged ? num_pages : 0;
+  const bool bf16 = dtype == GQA_BF16;
+  AppendFn fn = global ? pick_append<4, 512>(paged, bf16) : pick_append<16, 256>(paged, bf16);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  ProfRec* pr = prof_slot(4 + variant);
+  if (pr) hipEventRecord(pr->start, stream);
+  const unsigned rows = kHeads + 2 * (global ? 4 : 16);  // q, k and v head rows
+  hipLaunchKernelGGL(fn, dim3((unsigned)B, (rows + kWaves - 1) / kWaves), dim3(kThreads), 0, stream,
+                     aa);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  if (pr) hipEventRecord(pr->stop, stream);
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1044,6 +1270,37 @@ int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, 
   if (n_waves) *n_waves = p.waves;
   if (n_slots) *n_slots = p.slots;
   return GQA_OK;
+}
+
+int gqa_append_sliding(const void* q_raw, const void* k_raw, const void* v_raw, const void* w_q,
+                       const void* w_k, const int32_t* seq_lens, void* q_out, void* k_cache,
+                       void* v_cache, int32_t B, int32_t S_max, int32_t dtype, void* stream) {
+  return run_append(GQA_SLIDING, false, q_raw, k_raw, v_raw, w_q, w_k, nullptr, 0, seq_lens, q_out,
+                    k_cache, v_cache, B, S_max, 0, dtype, stream);
+}
+
+int gqa_append_sliding_paged(const void* q_raw, const void* k_raw, const void* v_raw,
+                             const void* w_q, const void* w_k, const int32_t* block_table,
+                             int32_t max_pages, const int32_t* seq_lens, void* q_out,
+                             void* k_pool, void* v_pool, int32_t B, int32_t num_pages,
+                             int32_t dtype, void* stream) {
+  return run_append(GQA_SLIDING, true, q_raw, k_raw, v_raw, w_q, w_k, block_table, max_pages,
+                    seq_lens, q_out, k_pool, v_pool, B, 0, num_pages, dtype, stream);
+}
+
+int gqa_append_global(const void* q_raw, const void* k_raw, const void* w_q, const void* w_k,
+                      const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache,
+                      int32_t B, int32_t S_max, int32_t dtype, void* stream) {
+  return run_append(GQA_GLOBAL, false, q_raw, k_raw, nullptr, w_q, w_k, nullptr, 0, seq_lens,
+                    q_out, k_cache, v_cache, B, S_max, 0, dtype, stream);
+}
+
+int gqa_append_global_paged(const void* q_raw, const void* k_raw, const void* w_q,
+                            const void* w_k, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, void* q_out, void* k_pool, void* v_pool,
+                            int32_t B, int32_t num_pages, int32_t dtype, void* stream) {
+  return run_append(GQA_GLOBAL, true, q_raw, k_raw, nullptr, w_q, w_k, block_table, max_pages,
+                    seq_lens, q_out, k_pool, v_pool, B, 0, num_pages, dtype, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity) {

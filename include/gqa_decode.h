@@ -130,6 +130,43 @@ size_t gqa_decode_sliding_window_workspace_bytes(int32_t B, int32_t capacity, in
 int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, int32_t* mode,
                                    int32_t* n_waves, int32_t* n_slots);
 
+/* KV append of the new token with its per-head norms and RoPE: the nodes
+ * attn.qk_norm, attn.v_norm and attn.rope of the Model Spec page's
+ * "Compute-graph nodes" table, applied to one new token per sequence at
+ * position pos = seq_lens[b] - 1 (seq_lens already counts the new token: the
+ * compact forward pass of the architecture page appends K/V before
+ * attention), then written into the cache at pos:
+ *   q_out[b,h]      = rope(q_raw[b,h] / rms * w_q)
+ *   cache k[b,pos,g] = rope(k_raw[b,g] / rms * w_k)
+ *   cache v[b,pos,g] = v_raw[b,g] / rms          (global: v_raw is k_raw)
+ *   rms = sqrt(mean_d x^2 + 1e-6); rope rotates pairs (i, i + D/2) by
+ *   pos * theta^(-2i/D), (a, b) -> (a cos - b sin, a sin + b cos), for
+ *   i < active: sliding theta 1e4, 128 of 128 pairs; global theta 1e6, the
+ *   first 64 of 256 pairs (the rest keep zero inverse frequency).
+ * Layouts: q_raw, q_out [B,32,D]; k_raw, v_raw [B,KV,D]; w_q, w_k [D]; caches
+ * as in the attention calls.  All share `dtype`; q_out may equal q_raw.
+ * Angles are formed in double precision, norms and rotation in fp32, outputs
+ * rounded to the dtype (RNE).  A sequence with seq_lens[b] outside
+ * [1, capacity] gets zero q_out rows and no cache write; a page id outside
+ * [0, num_pages) gets no cache write.  Nothing else in the cache is touched.
+ * Host-checked errors as for the attention calls (pointers, B, capacity,
+ * dtype, 16-byte alignment). */
+int gqa_append_sliding(const void* q_raw, const void* k_raw, const void* v_raw, const void* w_q,
+                       const void* w_k, const int32_t* seq_lens, void* q_out, void* k_cache,
+                       void* v_cache, int32_t B, int32_t S_max, int32_t dtype, void* stream);
+int gqa_append_sliding_paged(const void* q_raw, const void* k_raw, const void* v_raw,
+                             const void* w_q, const void* w_k, const int32_t* block_table,
+                             int32_t max_pages, const int32_t* seq_lens, void* q_out,
+                             void* k_pool, void* v_pool, int32_t B, int32_t num_pages,
+                             int32_t dtype, void* stream);
+int gqa_append_global(const void* q_raw, const void* k_raw, const void* w_q, const void* w_k,
+                      const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache,
+                      int32_t B, int32_t S_max, int32_t dtype, void* stream);
+int gqa_append_global_paged(const void* q_raw, const void* k_raw, const void* w_q,
+                            const void* w_k, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, void* q_out, void* k_pool, void* v_pool,
+                            int32_t B, int32_t num_pages, int32_t dtype, void* stream);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:
@@ -173,7 +210,8 @@ int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
  * `capacity` launches are kept).  gqa_profile_read synchronises those events
  * and reports, per kernel kind, the number of launches and their summed
  * duration in milliseconds (kind 2*variant: main kernel of that variant,
- * 2*variant+1: its combine kernel); it also disables recording and releases
+ * 2*variant+1: its combine kernel, 4+variant: its append kernel); it also
+ * disables recording and releases
  * the events.  Measurement only: not thread-safe, not for captured graphs. */
 int gqa_profile_begin(int32_t capacity);
 int gqa_profile_read(int32_t* counts, double* total_ms, int32_t n_kinds);

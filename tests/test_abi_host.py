@@ -151,6 +151,20 @@ def test_window_arguments(lib):
         gqa.gqa_decode_plan("global", 4, 4096, window=1024)
 
 
+def test_append_arguments_fail_before_launch(lib):
+    P = ctypes.c_void_p
+    ok, mis = P(0x10000), P(0x10008)
+    sl, gl = lib.gqa_append_sliding, lib.gqa_append_global_paged
+    assert sl(ok, ok, None, ok, ok, ok, ok, ok, ok, 4, 64, 1, None) == -1   # sliding needs v_raw
+    assert sl(ok, ok, ok, ok, ok, ok, ok, ok, ok, 0, 64, 1, None) == -2
+    assert sl(ok, ok, ok, ok, ok, ok, ok, ok, ok, 4, 262145, 1, None) == -2
+    assert sl(ok, ok, ok, ok, ok, ok, ok, ok, ok, 4, 64, 7, None) == -3
+    assert sl(ok, ok, ok, mis, ok, ok, ok, ok, ok, 4, 64, 1, None) == -4
+    assert gl(ok, ok, ok, ok, None, 8, ok, ok, ok, ok, 4, 8, 1, None) == -1
+    assert gl(ok, ok, ok, ok, ok, 0, ok, ok, ok, ok, 4, 8, 1, None) == -2
+    assert gl(ok, ok, ok, ok, ok, 8, ok, ok, ok, mis, 4, 8, 1, None) == -4
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     q = torch.zeros(1, 32, 256, dtype=torch.bfloat16)
