@@ -67,6 +67,9 @@ def load(path: str = LIBRARY):
     fn.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, i32,
                    p, i32]
     fn.restype = ctypes.c_int
+    kv = lib.oracle_gqa_decode_k_from_v
+    kv.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, p, i32, p, i32]
+    kv.restype = ctypes.c_int
     ap = lib.oracle_gqa_append_rows
     ap.argtypes = [ctypes.c_int, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
     ap.restype = ctypes.c_int
@@ -172,3 +175,45 @@ def gqa_append_rows(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, lib=None):
     if rc != 0:
         raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
     return q_out, k_row, v_row, pos
+
+
+def gqa_decode_k_from_v(q, v, w_k, seq_lens, block_table=None, num_pages=None, rows=None,
+                        nthreads: int | None = None, lib=None) -> np.ndarray:
+    """decodeGQA over a values-only cache: the key of position s is
+    rope(w_k * v_s, s) (values = keys on the global layers), in fp64.
+
+    q [B,32,512]; v [B,S,4,512] or [num_pages,16,4,512] with block_table; w_k [512].
+    """
+    lib = lib or load()
+    q, v, w_k = (np.ascontiguousarray(a) for a in (q, v, w_k))
+    dt = _dtype_code(q)
+    if _dtype_code(v) != dt or _dtype_code(w_k) != dt:
+        raise TypeError("q, v, w_k must share a dtype")
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = q.shape[0]
+    if q.shape != (B, HEADS, 512) or w_k.shape != (512,) or seq_lens.shape != (B,):
+        raise ValueError("bad shapes")
+    if block_table is None:
+        if v.ndim != 4 or v.shape[0] != B or v.shape[2:] != (4, 512):
+            raise ValueError("v must be [B,S,4,512]")
+        cap, max_pages, n_pages, bt = v.shape[1], 0, 0, None
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if v.ndim != 4 or v.shape[1:] != (PAGE, 4, 512):
+            raise ValueError("paged v must be [num_pages,16,4,512]")
+        max_pages = bt.shape[1]
+        n_pages = v.shape[0] if num_pages is None else num_pages
+        cap = max_pages * PAGE
+    if rows is None:
+        rows_arr, n_rows = None, B * HEADS
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, 512), dtype=np.float64)
+    nthreads = nthreads or min(os.cpu_count() or 1, 16)
+    rc = lib.oracle_gqa_decode_k_from_v(dt, _ptr(q), _ptr(v), _ptr(w_k), _ptr(seq_lens), _ptr(bt),
+                                        B, cap, max_pages, n_pages, _ptr(rows_arr), n_rows,
+                                        _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
+    return out.reshape(B, HEADS, 512) if rows is None else out

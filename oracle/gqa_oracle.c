@@ -59,6 +59,7 @@ typedef struct {
   const int32_t *seq_lens;
   const int32_t *block_table; /* NULL: contiguous cache */
   int32_t B, cap, max_pages, num_pages, KV, D, window;
+  const void *w_k;     /* non-NULL: keys rebuilt from values (global layers) */
   const int32_t *rows; /* (b, h) pairs or NULL for every row */
   int32_t n_rows;
   double *out;
@@ -87,6 +88,16 @@ static int64_t orc_row_offset(const orc_job *j, int b, int64_t s, int g) {
   return (((int64_t)page * ORC_PAGE + s % ORC_PAGE) * j->KV + g) * (int64_t)j->D;
 }
 
+static void orc_rope(double *y, int D, long pos, double theta, int active);
+
+/* Key row of position s when keys are rebuilt from values (decodeGQA layers
+ * store values only, keys = values on those layers): k = rope(w_k * v, s). */
+static void orc_key_from_value(const orc_job *j, int64_t off, int64_t s, double *k) {
+  for (int d = 0; d < j->D; ++d)
+    k[d] = orc_elem(j->w_k, j->dtype, (size_t)d) * orc_elem(j->v, j->dtype, (size_t)off + d);
+  orc_rope(k, j->D, (long)s, 1e6, 64);
+}
+
 /* One output row o[b,h,:] written to out[0:D]. */
 static int orc_one_row(const orc_job *j, int b, int h, double *out) {
   const int D = j->D;
@@ -99,7 +110,7 @@ static int orc_one_row(const orc_job *j, int b, int h, double *out) {
   const int64_t lo = (j->window > 0 && L > j->window) ? L - j->window : 0;
   const int64_t n = L - lo;
 
-  double *z = (double *)malloc((size_t)n * sizeof(double));
+  double *z = (double *)malloc(((size_t)n + (size_t)D) * sizeof(double));
   if (!z) return ORC_ERR_NOMEM;
   const size_t qoff = ((size_t)b * ORC_HEADS + h) * (size_t)D;
 
@@ -108,8 +119,14 @@ static int orc_one_row(const orc_job *j, int b, int h, double *out) {
     int64_t off = orc_row_offset(j, b, s, g);
     if (off < 0) { free(z); return ORC_ERR_PAGE; }
     double acc = 0.0;
-    for (int d = 0; d < D; ++d)
-      acc += orc_elem(j->q, j->dtype, qoff + d) * orc_elem(j->k, j->dtype, (size_t)off + d);
+    if (j->w_k) {
+      double *krow = z + n; /* scratch after the logits */
+      orc_key_from_value(j, off, s, krow);
+      for (int d = 0; d < D; ++d) acc += orc_elem(j->q, j->dtype, qoff + d) * krow[d];
+    } else {
+      for (int d = 0; d < D; ++d)
+        acc += orc_elem(j->q, j->dtype, qoff + d) * orc_elem(j->k, j->dtype, (size_t)off + d);
+    }
     z[s - lo] = acc;
   }
   /* softmax over the window */
@@ -175,14 +192,15 @@ static void *orc_worker(void *arg) {
  *   nthreads     worker threads (>= 1)
  * Returns 0 or a negative ORC_ERR_* code.
  */
-int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
+static int orc_decode(int dtype, const void *q, const void *k, const void *v, const void *w_k,
                       const int32_t *seq_lens, const int32_t *block_table, int32_t B,
-                      int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV,
-                      int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
-                      double *out, int32_t nthreads) {
-  if (!q || !k || !v || !seq_lens || !out) return ORC_ERR_ARG;
+                      int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV, int32_t D,
+                      int32_t window, const int32_t *rows, int32_t n_rows, double *out,
+                      int32_t nthreads) {
+  if (!q || !(k || w_k) || !v || !seq_lens || !out) return ORC_ERR_ARG;
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
   if (B < 1 || cap < 1 || KV < 1 || ORC_HEADS % KV != 0 || D < 1) return ORC_ERR_ARG;
+  if (w_k && !(KV == 4 && D == 512)) return ORC_ERR_ARG;
   if (block_table && (max_pages < 1 || num_pages < 1 || cap != max_pages * ORC_PAGE))
     return ORC_ERR_ARG;
   if (!rows) n_rows = B * ORC_HEADS;
@@ -192,7 +210,7 @@ int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
 
   orc_job j;
   memset(&j, 0, sizeof j);
-  j.dtype = dtype; j.q = q; j.k = k; j.v = v;
+  j.dtype = dtype; j.q = q; j.k = k; j.v = v; j.w_k = w_k;
   j.seq_lens = seq_lens; j.block_table = block_table;
   j.B = B; j.cap = cap; j.max_pages = max_pages; j.num_pages = num_pages;
   j.KV = KV; j.D = D; j.window = window;
@@ -207,6 +225,49 @@ int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
   for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
   pthread_mutex_destroy(&j.mu);
   return j.err;
+}
+
+/*
+ * oracle_gqa_decode
+ *   dtype        ORC_F32 or ORC_BF16 (q, k, v share it)
+ *   q            [B, 32, D]
+ *   k, v         contiguous: [B, cap, KV, D]; paged: [num_pages, 16, KV, D]
+ *   seq_lens     [B] int32
+ *   block_table  NULL (contiguous) or [B, max_pages] int32 (paged; cap must
+ *                then equal max_pages*16)
+ *   KV, D        16/256 for slidingDecodeGQA, 4/512 for decodeGQA
+ *   window       1024 for slidingDecodeGQA, <= 0 for no window
+ *   rows         n_rows (b, h) pairs, or NULL for all B*32 rows in order
+ *   out          [n_rows, D] doubles
+ *   nthreads     worker threads (>= 1)
+ * Returns 0 or a negative ORC_ERR_* code.
+ */
+int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
+                      const int32_t *seq_lens, const int32_t *block_table, int32_t B,
+                      int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV,
+                      int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
+                      double *out, int32_t nthreads) {
+  return orc_decode(dtype, q, k, v, NULL, seq_lens, block_table, B, cap, max_pages, num_pages,
+                    KV, D, window, rows, n_rows, out, nthreads);
+}
+
+/*
+ * oracle_gqa_decode_k_from_v -- decodeGQA over a cache that stores values
+ * only.  On the global layers values are keys (Model Spec page, "What to
+ * watch for": values = keys; its attn.qk_norm / attn.v_norm / attn.rope rows:
+ * v = v_norm(x), k = rope(qk_norm(x) with weight w_k)), so the key of cached
+ * position s is k_s = rope(w_k * v_s, s) with theta 1e6 over the first 64 of
+ * the 256 pairs (i, i+256).  Arguments as oracle_gqa_decode with KV = 4,
+ * D = 512, the value cache in v and the weight w_k [512] (same dtype).
+ */
+int oracle_gqa_decode_k_from_v(int dtype, const void *q, const void *v, const void *w_k,
+                               const int32_t *seq_lens, const int32_t *block_table, int32_t B,
+                               int32_t cap, int32_t max_pages, int32_t num_pages,
+                               const int32_t *rows, int32_t n_rows, double *out,
+                               int32_t nthreads) {
+  if (!w_k) return ORC_ERR_ARG;
+  return orc_decode(dtype, q, NULL, v, w_k, seq_lens, block_table, B, cap, max_pages, num_pages,
+                    4, 512, 0, rows, n_rows, out, nthreads);
 }
 
 /*
