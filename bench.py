@@ -338,6 +338,37 @@ def main():
         app[name] = {"B": case.B, "us_per_call": round(ms * 1e3, 2), "bytes_per_call": moved,
                      "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
     line["config"]["append"] = app
+    log("decodeGQA over the values-only cache (keys rebuilt from values), global B=32 paged")
+    o_kv = torch.empty_like(gl.q)
+
+    def kfv_call():
+        gqa.gqa_decode_global_k_eq_v_paged(gl.q, gl.v, gl.w_k, gl.block_table, gl.seq_lens,
+                                           o=o_kv, workspace=ws_gl, stream=stream)
+
+    for _ in range(2):
+        kfv_call()
+    reps = max(3, min(args.steps, 10))
+    gqa.profile_begin(2 * reps + 4)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record(stream)
+    for _ in range(reps):
+        kfv_call()
+    b_ev.record(stream)
+    torch.cuda.synchronize()
+    kprof = gqa.profile_read()
+    ms = a_ev.elapsed_time(b_ev) / reps
+    k_main = kprof[("global_k_eq_v", "main")]
+    k_comb = kprof[("global_k_eq_v", "combine")]
+    kv_only = gl_bytes // 2  # the value rows only
+    line["config"]["global_k_eq_v"] = {
+        "cache": "paged16, values only", "v_bytes_per_call": kv_only,
+        "us_per_call": round(ms * 1e3, 2),
+        "main_kernel_us": round(k_main[1] / max(k_main[0], 1) * 1e3, 2),
+        "combine_kernel_us": round(k_comb[1] / max(k_comb[0], 1) * 1e3, 2),
+        "v_GBps": round(kv_only / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(kv_only / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "speedup_vs_stored_keys": round(gl_ms / ms, 3) if ms else None,
+    }
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
     line["roofline"]["measured_read_stream_GBps"] = probes["read_GBps"]

@@ -15,11 +15,17 @@ the library is missing or no GPU is present the calls raise.
     gqa_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
     gqa_append_global(q_raw, k_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
                                                         new token: norms, RoPE, cache write
+    gqa_decode_global_k_eq_v(q, v, w_k, seq_lens)       decodeGQA over a values-only cache
+    gqa_decode_global_k_eq_v_paged(q, v_pool, w_k, block_table, seq_lens)
+    gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache[, block_table])
 
 Shapes (attn.core of the gemma-4-31B Model Spec page): q [B,32,D]; contiguous
 k/v [B,S_max,KV,D]; paged pools [num_pages,16,KV,D] with block_table
 [B,max_pages] int32; seq_lens [B] int32; returns o [B,32,D] of q's dtype
 (float32 or bfloat16).  Sliding: KV=16, D=256, window 1024.  Global: KV=4, D=512.
+The values-only variants keep one [.,.,4,512] cache for the global layers,
+whose values equal their keys before RoPE and the k weight: the key of
+position s is rope(w_k * v_s, s), rebuilt inside the attention kernel.
 """
 from __future__ import annotations
 
@@ -31,8 +37,11 @@ from ._lib import (  # noqa: F401
     GqaError,
     constants,
     gqa_append_global,
+    gqa_append_global_k_eq_v,
     gqa_append_sliding,
     gqa_decode_global,
+    gqa_decode_global_k_eq_v,
+    gqa_decode_global_k_eq_v_paged,
     gqa_decode_global_paged,
     gqa_decode_plan,
     gqa_decode_sliding,

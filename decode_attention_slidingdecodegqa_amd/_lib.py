@@ -21,7 +21,9 @@ EXPORTED_SYMBOLS = (
     "gqa_hbm_read_probe", "gqa_hbm_copy_probe", "gqa_decode_sliding_window",
     "gqa_decode_sliding_window_paged", "gqa_decode_sliding_window_workspace_bytes",
     "gqa_decode_sliding_window_plan", "gqa_append_sliding", "gqa_append_sliding_paged",
-    "gqa_append_global", "gqa_append_global_paged",
+    "gqa_append_global", "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
+    "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
+    "gqa_append_global_k_eq_v_paged",
 )
 
 
@@ -63,8 +65,15 @@ def library():
     lib.gqa_append_sliding_paged.argtypes = [p, p, p, p, p, p, i32, p, p, p, p, i32, i32, i32, p]
     lib.gqa_append_global.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, p]
     lib.gqa_append_global_paged.argtypes = [p, p, p, p, p, i32, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_decode_global_k_eq_v.argtypes = [p, p, p, p, p, i32, i32, i32, p, sz, p]
+    lib.gqa_decode_global_k_eq_v_paged.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, p, sz,
+                                                   p]
+    lib.gqa_append_global_k_eq_v.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_append_global_k_eq_v_paged.argtypes = [p, p, p, p, p, i32, p, p, p, i32, i32, i32, p]
     for name in ("gqa_append_sliding", "gqa_append_sliding_paged", "gqa_append_global",
-                 "gqa_append_global_paged"):
+                 "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
+                 "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
+                 "gqa_append_global_k_eq_v_paged"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32]
     lib.gqa_decode_workspace_bytes.restype = sz
@@ -140,17 +149,21 @@ def profile_begin(capacity: int) -> None:
 
 
 def profile_read() -> dict:
-    """{(variant, kernel): (launches, total_ms)} for variant in sliding/global and
-    kernel in main/combine/append."""
-    counts = (ctypes.c_int32 * 6)()
-    ms = (ctypes.c_double * 6)()
-    rc = library().gqa_profile_read(counts, ms, 6)
+    """{(variant, kernel): (launches, total_ms)} for variant in sliding / global /
+    global_k_eq_v (global layers over a values-only cache) and kernel in
+    main/combine/append."""
+    n = 9
+    counts = (ctypes.c_int32 * n)()
+    ms = (ctypes.c_double * n)()
+    rc = library().gqa_profile_read(counts, ms, n)
     if rc:
         raise GqaError("gqa_profile_read", rc)
     out = {}
     for vi, vname in enumerate(("sliding", "global")):
         for kind, kname in ((2 * vi, "main"), (2 * vi + 1, "combine"), (4 + vi, "append")):
             out[(vname, kname)] = (counts[kind], ms[kind])
+    for kind, kname in ((6, "main"), (7, "combine"), (8, "append")):
+        out[("global_k_eq_v", kname)] = (counts[kind], ms[kind])
     return out
 
 
@@ -362,3 +375,90 @@ def gqa_append_global(q_raw, k_raw, w_q, w_k, seq_lens, k_cache, v_cache, block_
     """As gqa_append_sliding for the global layers (values = keys: no v_raw)."""
     return _append_call(GQA_GLOBAL, q_raw, k_raw, None, w_q, w_k, seq_lens, k_cache, v_cache,
                         block_table, q_out, stream)
+
+
+def _check_w_k(w_k, q):
+    if w_k.shape != (512,) or w_k.dtype != q.dtype:
+        raise ValueError("w_k must be [512] in the dtype of q")
+
+
+def gqa_decode_global_k_eq_v(q, v, w_k, seq_lens, o=None, workspace=None, stream=None):
+    """decodeGQA over a values-only cache v [B,S_max,4,512]: the key of position
+    s is rope(w_k * v_s, s), rebuilt in the kernel (values = keys)."""
+    if v.dim() != 4 or v.shape[0] != q.shape[0] or v.shape[2:] != (4, 512):
+        raise ValueError("v must be [B,S_max,4,512]")
+    if q.dtype != v.dtype:
+        raise TypeError("q and v must share a dtype")
+    _check_w_k(w_k, q)
+    S_max = v.shape[1]
+    B, o, ws, ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, S_max)
+    name = "gqa_decode_global_k_eq_v"
+    rc = getattr(library(), name)(_dev(q, "q"), _dev(v, "v"), _dev(w_k, "w_k"),
+                                  _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, S_max,
+                                  _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    if rc:
+        raise GqaError(name, rc)
+    return o
+
+
+def gqa_decode_global_k_eq_v_paged(q, v_pool, w_k, block_table, seq_lens, o=None,
+                                   workspace=None, stream=None):
+    """As gqa_decode_global_k_eq_v on a paged values-only pool [num_pages,16,4,512]."""
+    if v_pool.dim() != 4 or v_pool.shape[1:] != (PAGE, 4, 512):
+        raise ValueError("v_pool must be [num_pages,16,4,512]")
+    if q.dtype != v_pool.dtype:
+        raise TypeError("q and v_pool must share a dtype")
+    _check_w_k(w_k, q)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table must be int32 [B,max_pages]")
+    max_pages = block_table.shape[1]
+    B, o, ws, ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, max_pages * PAGE)
+    name = "gqa_decode_global_k_eq_v_paged"
+    rc = getattr(library(), name)(_dev(q, "q"), _dev(v_pool, "v_pool"), _dev(w_k, "w_k"),
+                                  _dev(block_table, "block_table"), max_pages,
+                                  _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, v_pool.shape[0],
+                                  _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    if rc:
+        raise GqaError(name, rc)
+    return o
+
+
+def gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache, block_table=None,
+                             q_out=None, stream=None):
+    """Append of the global layers to a values-only cache: writes q_out (returned)
+    and the unit-RMS value row of the new token; no key row is stored."""
+    B = q_raw.shape[0]
+    if q_raw.shape != (B, HEADS, 512) or k_raw.shape != (B, 4, 512):
+        raise ValueError("q_raw must be [B,32,512] and k_raw [B,4,512]")
+    if w_q.shape != (512,) or w_k.shape != (512,):
+        raise ValueError("w_q and w_k must be [512]")
+    if len({t.dtype for t in (q_raw, k_raw, w_q, w_k, v_cache)}) != 1:
+        raise TypeError("inputs, weights and cache must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if q_out is None:
+        q_out = torch.empty_like(q_raw)
+    lib = library()
+    st = _stream(stream, q_raw.device)
+    ptrs = [_dev(q_raw, "q_raw"), _dev(k_raw, "k_raw"), _dev(w_q, "w_q"), _dev(w_k, "w_k")]
+    dt = _dtype_code(q_raw)
+    if block_table is None:
+        name = "gqa_append_global_k_eq_v"
+        if v_cache.dim() != 4 or v_cache.shape[0] != B or v_cache.shape[2:] != (4, 512):
+            raise ValueError("v_cache must be [B,S_max,4,512]")
+        rc = getattr(lib, name)(*ptrs, _dev(seq_lens, "seq_lens"), _dev(q_out, "q_out"),
+                                _dev(v_cache, "v_cache"), B, v_cache.shape[1], dt, st)
+    else:
+        name = "gqa_append_global_k_eq_v_paged"
+        if v_cache.dim() != 4 or v_cache.shape[1:] != (PAGE, 4, 512):
+            raise ValueError("v_pool must be [num_pages,16,4,512]")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B,max_pages]")
+        rc = getattr(lib, name)(*ptrs, _dev(block_table, "block_table"), block_table.shape[1],
+                                _dev(seq_lens, "seq_lens"), _dev(q_out, "q_out"),
+                                _dev(v_cache, "v_pool"), B, v_cache.shape[0], dt, st)
+    if rc:
+        raise GqaError(name, rc)
+    return q_out

@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "gqa_decode.h"
@@ -84,8 +85,9 @@ struct Elem<false> {
 
 struct KernelArgs {
   const char* q;
-  const char* k;
+  const char* k;    // unused when keys are rebuilt from values
   const char* v;
+  const char* w_k;  // key weight [512]: keys rebuilt from values (global layers) when set
   const int32_t* seq_lens;
   const int32_t* block_table;
   char* o;
@@ -206,14 +208,67 @@ struct WaveState {
   float l;                     // this lane's share of the sum of weights
 };
 
+// ---- keys rebuilt from values (global layers: values = keys)
+// k_s = rope(w_k * v_s, s): pairs (i, i+256) rotate by s * 1e6^(-2i/512) for
+// i < 64, the other 448 coordinates are w_k * v.  The unrotated coordinates
+// fold w_k into the query once per unit; a rotated pair of position
+// pos0 + r is R(pos0*f_i) * M[r][i] * (v_i, v_{i+256}) with the work-group
+// table M[r][i] = R(r*f_i) * diag(w_i, w_{i+256}) (r < 16) and the wave's
+// per-tile base R(pos0*f_i), both in LDS, the angles formed in double.
+constexpr int kRopePairs = 64;
+constexpr double kLog2ThetaGlobal = 19.931568569324174;  // log2(1e6)
+
+struct RopeLds {
+  // R(r f_i) diag(w_i, w_{i+256}) as a row-major 2x2, pair-major so that the
+  // 16 rows of one pair are 16 consecutive 16-byte entries (no bank conflicts)
+  float m[kRopePairs][kTile][4];
+  float base[kWaves][kRopePairs][2];  // per wave: (cos, sin)(pos0 f_i)
+  double freq[kRopePairs];        // f_i = 1e6^(-2i/512)
+};
+
+template <bool BF16>
+__device__ inline float elem_f32(const char* base, int i) {
+  if constexpr (BF16) return bf16_value(*reinterpret_cast<const unsigned short*>(base + 2 * i));
+  return *reinterpret_cast<const float*>(base + 4 * i);
+}
+
+template <bool BF16>
+__device__ void rope_tables_init(const char* w_k, RopeLds* rl) {
+  for (int idx = threadIdx.x; idx < kTile * kRopePairs; idx += kThreads) {
+    const int r = idx / kRopePairs, i = idx % kRopePairs;
+    const double f = exp2(-2.0 * i / 512 * kLog2ThetaGlobal);
+    if (r == 0) rl->freq[i] = f;
+    double sd, cd;
+    sincos(r * f, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    const float wa = elem_f32<BF16>(w_k, i), wb = elem_f32<BF16>(w_k, i + 256);
+    rl->m[i][r][0] = c * wa;
+    rl->m[i][r][1] = -sn * wb;
+    rl->m[i][r][2] = sn * wa;
+    rl->m[i][r][3] = c * wb;
+  }
+}
+
+// the calling wave's base rotation of the tile starting at position pos0
+__device__ inline void rope_base(RopeLds* rl, int wave, int pos0) {
+  const int i = threadIdx.x & 63;
+  const double ang = (double)pos0 * rl->freq[i];
+  const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  float sn, c;
+  sincosf((float)red, &sn, &c);
+  rl->base[wave][i][0] = c;
+  rl->base[wave][i][1] = sn;
+}
+
 // Accumulates into st the tiles k_begin, k_begin + step, ... (< k_end) of unit
 // (b, g), whose attended range is sr, with the calling wave.  myq is the wave's
 // LDS slice for the unit's query heads.
-template <int KV, int D, bool PAGED, bool BF16>
+template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int g,
                                                  const SeqRange& sr, int k_begin, int k_end,
-                                                 int step, u32x4* myq,
+                                                 int step, u32x4* myq, RopeLds* rl,
                                                  WaveState<KV, D, BF16>& st) {
+  static_assert(!KFV || (KV == 4 && D == 512), "keys from values: global layers only");
   using Gm = Geo<KV, D, BF16>;
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
                 VBLK = Gm::VBLK, QPL = Gm::QPL;
@@ -245,6 +300,30 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     for (int i = 0; i < QPL; ++i) {
       const int c = lane + 64 * i;
       if (c < G * NCH) qstage[i] = load16(qsrc + (size_t)c * 16);
+    }
+    if constexpr (KFV) {
+      // w_k folded into the query on the coordinates that do not rotate
+#pragma unroll
+      for (int i = 0; i < QPL; ++i) {
+        const int c = lane + 64 * i;
+        const int cc = c % NCH;  // chunk within the head row
+        if (c < G * NCH && (cc * E) % 256 >= kRopePairs) {
+          const u32x4 w = load16(a.w_k + (size_t)cc * 16);
+          if constexpr (BF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const unsigned x = qstage[i][q], y = w[q];
+              const float lo = bf16_value(x & 0xffffu) * bf16_value(y & 0xffffu);
+              const float hi = bf16_value(x >> 16) * bf16_value(y >> 16);
+              qstage[i][q] = bf16_bits(lo) | (bf16_bits(hi) << 16);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              qstage[i][q] = __builtin_bit_cast(unsigned, chunk_f32(qstage[i], q) * chunk_f32(w, q));
+          }
+        }
+      }
     }
   }
   const u32x4* qrow = myq + (r < G ? r : 0) * NCH;
@@ -283,7 +362,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       ta.ok = true;
       off = (((size_t)b * a.cap + ta.pos0) * KV + g) * (size_t)ROW;
     }
-    ta.kb = a.k + off;
+    ta.kb = (KFV ? a.v : a.k) + off;
     ta.vb = a.v + off;
     return ta;
   };
@@ -309,9 +388,72 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     }
   };
 
+  // keys rebuilt from the value row in kreg: the lane's rotated pairs are
+  // chunks t < TA (coordinates < 64) and their partners t + TP (+256)
+  auto rebuild_keys = [&]() {
+    if constexpr (KFV) {
+      constexpr int TA = kRopePairs / (4 * E), TP = 256 / (4 * E);
+      // position within the tile, opaque to the optimizer: the M entries are
+      // loop-invariant and would otherwise be hoisted out of the tile loop
+      // into 64 registers this kernel does not have
+      int rr = lane & 15;
+      asm volatile("" : "+v"(rr));
+      const int wave = threadIdx.x >> 6;
+#pragma unroll
+      for (int t = 0; t < TA; ++t) {
+        float va[E], vb[E];
+        if constexpr (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            va[2 * q] = bf16_value(kreg[t][q] & 0xffffu);
+            va[2 * q + 1] = bf16_value(kreg[t][q] >> 16);
+            vb[2 * q] = bf16_value(kreg[t + TP][q] & 0xffffu);
+            vb[2 * q + 1] = bf16_value(kreg[t + TP][q] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            va[e] = chunk_f32(kreg[t], e);
+            vb[e] = chunk_f32(kreg[t + TP], e);
+          }
+        }
+        // four pairs at a time: the scheduler barrier bounds the LDS reads in
+        // flight (registers are the scarce resource of this kernel)
+#pragma unroll
+        for (int e0 = 0; e0 < E; e0 += 4) {
+#pragma unroll
+          for (int e = e0; e < e0 + 4; ++e) {
+            const int i = E * (4 * t + j) + e;  // pair index
+            const f32x4 M = *reinterpret_cast<const f32x4*>(rl->m[i][rr]);
+            const f32x2 Bs = *reinterpret_cast<const f32x2*>(rl->base[wave][i]);
+            const float xa = M[0] * va[e] + M[1] * vb[e];
+            const float xb = M[2] * va[e] + M[3] * vb[e];
+            va[e] = Bs[0] * xa - Bs[1] * xb;
+            vb[e] = Bs[1] * xa + Bs[0] * xb;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            kreg[t][q] = bf16_bits(va[2 * q]) | (bf16_bits(va[2 * q + 1]) << 16);
+            kreg[t + TP][q] = bf16_bits(vb[2 * q]) | (bf16_bits(vb[2 * q + 1]) << 16);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            kreg[t][e] = __builtin_bit_cast(unsigned, va[e]);
+            kreg[t + TP][e] = __builtin_bit_cast(unsigned, vb[e]);
+          }
+        }
+      }
+    }
+  };
+
   TileAt cur = tile_at(0);
   load_k(cur);
   load_v(cur);
+  if constexpr (KFV) rope_base(rl, threadIdx.x >> 6, cur.pos0);
 #pragma unroll
   for (int i = 0; i < QPL; ++i) {
     const int c = lane + 64 * i;
@@ -324,6 +466,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   for (int it = 0; it < n_it; ++it) {
     const bool more = it + 1 < n_it;
     const TileAt nxt = more ? tile_at(it + 1) : cur;
+
+    rebuild_keys();
 
     // logits z[pos 4j+i][head r]
     f32x4 z;
@@ -356,6 +500,14 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     }
     // the key registers are free: fetch the next tile's keys
     if (more) load_k(nxt);
+    if constexpr (KFV) {
+      if (more) {
+        // the base of the next tile (this tile's rebuilt keys no longer read it)
+        rope_base(rl, threadIdx.x >> 6, nxt.pos0);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -477,7 +629,7 @@ __device__ __forceinline__ void store_partial(const WaveState<KV, D, BF16>& st, 
 }
 
 // ---- stream kernel: W persistent waves, each an equal slice of all tiles
-template <int KV, int D, bool PAGED, bool BF16>
+template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_stream_kernel(
     KernelArgs a) {
   using Gm = Geo<KV, D, BF16>;
@@ -493,6 +645,9 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ int s_cnt[kMaxBatch];         // tiles per unit of the sequence
   __shared__ int s_before[kMaxBatch + 1];  // tiles per unit summed over earlier sequences
   __shared__ u32x4 s_q[kWaves][G * NCH];   // per-wave query heads of the current unit
+  __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
+  RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
+  if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
   if (threadIdx.x < 64) {
     int cnt[4];
 #pragma unroll
@@ -561,7 +716,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
     const SeqRange sr = seq_range(s_len[b], a.cap, a.window);
     const int k_begin = kk0;
     const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
-    accumulate_tiles<KV, D, PAGED, BF16>(a, b, g, sr, k_begin, k_end, 1, s_q[threadIdx.x >> 6], st);
+    accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin, k_end, 1,
+                                               s_q[threadIdx.x >> 6], s_rope, st);
 
     // the wave writes o when its slice holds the whole unit, else a partial
     if (r < G) {
@@ -590,7 +746,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
 
 // ---- unit kernel: one work-group per unit (many short units); its four
 // waves take interleaved tiles and merge their states in LDS, then write o
-template <int KV, int D, bool PAGED, bool BF16>
+template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_unit_kernel(
     KernelArgs a) {
   using Gm = Geo<KV, D, BF16>;
@@ -600,6 +756,12 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ float s_acc[(kWaves - 1) * G * LROW];
   __shared__ float s_m[(kWaves - 1) * G];
   __shared__ float s_l[(kWaves - 1) * G];
+  __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
+  RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
+  if constexpr (KFV) {
+    rope_tables_init<BF16>(a.w_k, s_rope);
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -617,7 +779,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   }
 
   WaveState<KV, D, BF16> st;
-  accumulate_tiles<KV, D, PAGED, BF16>(a, b, g, sr, wave, sr.n, kWaves, s_q[wave], st);
+  accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, wave, sr.n, kWaves, s_q[wave], s_rope,
+                                            st);
 
   if (wave > 0 && r < G) {
     float* dst = s_acc + ((wave - 1) * G + r) * LROW;
@@ -773,7 +936,7 @@ struct AppendArgs {
   const int32_t* seq_lens;
   const int32_t* block_table;
   char* q_out;
-  char* k_cache;
+  char* k_cache;  // nullptr: values-only cache (global layers), no key row
   char* v_cache;
   int32_t B;
   int32_t cap;
@@ -874,6 +1037,7 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
   if (row < ROWS) {
     const bool is_q = row < kHeads;
     const bool is_k = !is_q && row < kHeads + KV;
+    if (is_k && a.k_cache == nullptr) return;  // values-only cache: no key row
     const int head = is_q ? row : (is_k ? row - kHeads : row - kHeads - KV);
     char* dst;
     const char* src;
@@ -1047,15 +1211,16 @@ inline ProfRec* prof_slot(int kind) {
 typedef void (*MainFn)(KernelArgs);
 typedef void (*CombineFn)(CombineArgs);
 
-template <int KV, int D>
+template <int KV, int D, bool KFV>
 MainFn pick_main(bool unit_mode, bool paged, bool bf16) {
   if (unit_mode) {
-    if (paged) return bf16 ? gqa_unit_kernel<KV, D, true, true> : gqa_unit_kernel<KV, D, true, false>;
-    return bf16 ? gqa_unit_kernel<KV, D, false, true> : gqa_unit_kernel<KV, D, false, false>;
+    if (paged)
+      return bf16 ? gqa_unit_kernel<KV, D, true, true, KFV> : gqa_unit_kernel<KV, D, true, false, KFV>;
+    return bf16 ? gqa_unit_kernel<KV, D, false, true, KFV> : gqa_unit_kernel<KV, D, false, false, KFV>;
   }
   if (paged)
-    return bf16 ? gqa_stream_kernel<KV, D, true, true> : gqa_stream_kernel<KV, D, true, false>;
-  return bf16 ? gqa_stream_kernel<KV, D, false, true> : gqa_stream_kernel<KV, D, false, false>;
+    return bf16 ? gqa_stream_kernel<KV, D, true, true, KFV> : gqa_stream_kernel<KV, D, true, false, KFV>;
+  return bf16 ? gqa_stream_kernel<KV, D, false, true, KFV> : gqa_stream_kernel<KV, D, false, false, KFV>;
 }
 
 template <int KV, int D>
@@ -1067,11 +1232,19 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int default_window(int variant) { return variant == GQA_SLIDING ? kSlidingWindow : 0; }
 
+// Profiling kinds: 2*variant main, 2*variant+1 combine, 4+variant append; the
+// global layers over a values-only cache: 6 main, 7 combine, 8 append.
+constexpr int kProfKeysFromValues = 6;
+
+// w_k != nullptr: global layers over a values-only cache (k unused, keys
+// rebuilt from v)
 int run(int variant, int window, bool paged, const void* q, const void* k, const void* v,
-        const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens, void* o,
-        int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype, void* workspace,
+        const void* w_k, const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+        void* o, int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype, void* workspace,
         size_t workspace_bytes_given, void* stream_) {
-  if (!q || !k || !v || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
+  const bool kfv = w_k != nullptr;
+  if (kfv && variant != GQA_GLOBAL) return GQA_ERR_DTYPE;
+  if (!q || (!k && !kfv) || !v || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
   if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
   if (B < 1 || B > kMaxBatch) return GQA_ERR_SHAPE;
   int cap;
@@ -1082,7 +1255,8 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
     if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
     cap = S_max;
   }
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(w_k))
+    return GQA_ERR_ALIGN;
   VariantInfo vi;
   variant_info(variant, &vi);
   Plan plan;
@@ -1101,6 +1275,7 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ka.q = static_cast<const char*>(q);
   ka.k = static_cast<const char*>(k);
   ka.v = static_cast<const char*>(v);
+  ka.w_k = static_cast<const char*>(w_k);
   ka.seq_lens = seq_lens;
   ka.block_table = block_table;
   ka.o = static_cast<char*>(o);
@@ -1114,9 +1289,10 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ka.window = window;
   ka.n_waves = plan.waves;
 
-  MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256>(unit_mode, paged, bf16)
-                                          : pick_main<4, 512>(unit_mode, paged, bf16);
-  ProfRec* pr = prof_slot(2 * variant);
+  MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(unit_mode, paged, bf16)
+                   : kfv                   ? pick_main<4, 512, true>(unit_mode, paged, bf16)
+                                           : pick_main<4, 512, false>(unit_mode, paged, bf16);
+  ProfRec* pr = prof_slot(kfv ? kProfKeysFromValues : 2 * variant);
   if (pr) hipEventRecord(pr->start, stream);
   hipLaunchKernelGGL(main_fn, dim3((unsigned)(plan.waves / kWaves)), dim3(kThreads), 0, stream, ka);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
@@ -1132,7 +1308,7 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ca.n_waves = plan.waves;
   CombineFn comb =
       variant == GQA_SLIDING ? pick_combine<16, 256>(bf16) : pick_combine<4, 512>(bf16);
-  ProfRec* pc = prof_slot(2 * variant + 1);
+  ProfRec* pc = prof_slot(kfv ? kProfKeysFromValues + 1 : 2 * variant + 1);
   if (pc) hipEventRecord(pc->start, stream);
   hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3((unsigned)(vi.D / 4)), 0, stream, ca);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
@@ -1149,13 +1325,17 @@ AppendFn pick_append(bool paged, bool bf16) {
   return bf16 ? gqa_append_kernel<KV, D, false, true> : gqa_append_kernel<KV, D, false, false>;
 }
 
-int run_append(int variant, bool paged, const void* q_raw, const void* k_raw, const void* v_raw,
-               const void* w_q, const void* w_k, const int32_t* block_table, int32_t max_pages,
-               const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache, int32_t B,
-               int32_t S_max, int32_t num_pages, int32_t dtype, void* stream_) {
+// k_cache == nullptr with values_only: global layers over a values-only cache
+// (the key row is not written; attention rebuilds it from the value row)
+int run_append(int variant, bool paged, bool values_only, const void* q_raw, const void* k_raw,
+               const void* v_raw, const void* w_q, const void* w_k, const int32_t* block_table,
+               int32_t max_pages, const int32_t* seq_lens, void* q_out, void* k_cache,
+               void* v_cache, int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype,
+               void* stream_) {
   const bool global = variant == GQA_GLOBAL;
+  if (values_only && !global) return GQA_ERR_DTYPE;
   if (!q_raw || !k_raw || (!global && !v_raw) || !w_q || !w_k || !seq_lens || !q_out ||
-      !k_cache || !v_cache || (paged && !block_table))
+      (!k_cache && !values_only) || !v_cache || (paged && !block_table))
     return GQA_ERR_NULL;
   if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
   if (B < 1 || B > kMaxBatch) return GQA_ERR_SHAPE;
@@ -1180,7 +1360,7 @@ int run_append(int variant, bool paged, const void* q_raw, const void* k_raw, co
   aa.seq_lens = seq_lens;
   aa.block_table = block_table;
   aa.q_out = static_cast<char*>(q_out);
-  aa.k_cache = static_cast<char*>(k_cache);
+  aa.k_cache = values_only ? nullptr : static_cast<char*>(k_cache);
   aa.v_cache = static_cast<char*>(v_cache);
   aa.B = B;
   aa.cap = cap;
@@ -1189,7 +1369,7 @@ int run_append(int variant, bool paged, const void* q_raw, const void* k_raw, co
   const bool bf16 = dtype == GQA_BF16;
   AppendFn fn = global ? pick_append<4, 512>(paged, bf16) : pick_append<16, 256>(paged, bf16);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  ProfRec* pr = prof_slot(4 + variant);
+  ProfRec* pr = prof_slot(values_only ? kProfKeysFromValues + 2 : 4 + variant);
   if (pr) hipEventRecord(pr->start, stream);
   const unsigned rows = kHeads + 2 * (global ? 4 : 16);  // q, k and v head rows
   hipLaunchKernelGGL(fn, dim3((unsigned)B, (rows + kWaves - 1) / kWaves), dim3(kThreads), 0, stream,
@@ -1206,14 +1386,14 @@ extern "C" {
 int gqa_decode_sliding(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                        void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return run(GQA_SLIDING, kSlidingWindow, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
+  return run(GQA_SLIDING, kSlidingWindow, false, q, k, v, nullptr, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
              workspace_bytes, stream);
 }
 
 int gqa_decode_global(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                       void* o, int32_t B, int32_t S_max, int32_t dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return run(GQA_GLOBAL, 0, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
+  return run(GQA_GLOBAL, 0, false, q, k, v, nullptr, nullptr, 0, seq_lens, o, B, S_max, 0, dtype, workspace,
              workspace_bytes, stream);
 }
 
@@ -1222,7 +1402,7 @@ int gqa_decode_sliding_paged(const void* q, const void* k_pool, const void* v_po
                              const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
                              int32_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  return run(GQA_SLIDING, kSlidingWindow, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
+  return run(GQA_SLIDING, kSlidingWindow, true, q, k_pool, v_pool, nullptr, block_table, max_pages, seq_lens, o, B, 0,
              num_pages, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -1231,7 +1411,7 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
                             const int32_t* seq_lens, void* o, int32_t B, int32_t num_pages,
                             int32_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  return run(GQA_GLOBAL, 0, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B, 0,
+  return run(GQA_GLOBAL, 0, true, q, k_pool, v_pool, nullptr, block_table, max_pages, seq_lens, o, B, 0,
              num_pages, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -1240,7 +1420,7 @@ int gqa_decode_sliding_window(const void* q, const void* k, const void* v,
                               int32_t window, int32_t dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (window < 1) return GQA_ERR_SHAPE;
-  return run(GQA_SLIDING, window, false, q, k, v, nullptr, 0, seq_lens, o, B, S_max, 0, dtype,
+  return run(GQA_SLIDING, window, false, q, k, v, nullptr, nullptr, 0, seq_lens, o, B, S_max, 0, dtype,
              workspace, workspace_bytes, stream);
 }
 
@@ -1250,7 +1430,7 @@ int gqa_decode_sliding_window_paged(const void* q, const void* k_pool, const voi
                                     int32_t num_pages, int32_t window, int32_t dtype,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   if (window < 1) return GQA_ERR_SHAPE;
-  return run(GQA_SLIDING, window, true, q, k_pool, v_pool, block_table, max_pages, seq_lens, o, B,
+  return run(GQA_SLIDING, window, true, q, k_pool, v_pool, nullptr, block_table, max_pages, seq_lens, o, B,
              0, num_pages, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -1275,7 +1455,7 @@ int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, 
 int gqa_append_sliding(const void* q_raw, const void* k_raw, const void* v_raw, const void* w_q,
                        const void* w_k, const int32_t* seq_lens, void* q_out, void* k_cache,
                        void* v_cache, int32_t B, int32_t S_max, int32_t dtype, void* stream) {
-  return run_append(GQA_SLIDING, false, q_raw, k_raw, v_raw, w_q, w_k, nullptr, 0, seq_lens, q_out,
+  return run_append(GQA_SLIDING, false, false, q_raw, k_raw, v_raw, w_q, w_k, nullptr, 0, seq_lens, q_out,
                     k_cache, v_cache, B, S_max, 0, dtype, stream);
 }
 
@@ -1284,14 +1464,14 @@ int gqa_append_sliding_paged(const void* q_raw, const void* k_raw, const void* v
                              int32_t max_pages, const int32_t* seq_lens, void* q_out,
                              void* k_pool, void* v_pool, int32_t B, int32_t num_pages,
                              int32_t dtype, void* stream) {
-  return run_append(GQA_SLIDING, true, q_raw, k_raw, v_raw, w_q, w_k, block_table, max_pages,
+  return run_append(GQA_SLIDING, true, false, q_raw, k_raw, v_raw, w_q, w_k, block_table, max_pages,
                     seq_lens, q_out, k_pool, v_pool, B, 0, num_pages, dtype, stream);
 }
 
 int gqa_append_global(const void* q_raw, const void* k_raw, const void* w_q, const void* w_k,
                       const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache,
                       int32_t B, int32_t S_max, int32_t dtype, void* stream) {
-  return run_append(GQA_GLOBAL, false, q_raw, k_raw, nullptr, w_q, w_k, nullptr, 0, seq_lens,
+  return run_append(GQA_GLOBAL, false, false, q_raw, k_raw, nullptr, w_q, w_k, nullptr, 0, seq_lens,
                     q_out, k_cache, v_cache, B, S_max, 0, dtype, stream);
 }
 
@@ -1299,8 +1479,44 @@ int gqa_append_global_paged(const void* q_raw, const void* k_raw, const void* w_
                             const void* w_k, const int32_t* block_table, int32_t max_pages,
                             const int32_t* seq_lens, void* q_out, void* k_pool, void* v_pool,
                             int32_t B, int32_t num_pages, int32_t dtype, void* stream) {
-  return run_append(GQA_GLOBAL, true, q_raw, k_raw, nullptr, w_q, w_k, block_table, max_pages,
+  return run_append(GQA_GLOBAL, true, false, q_raw, k_raw, nullptr, w_q, w_k, block_table, max_pages,
                     seq_lens, q_out, k_pool, v_pool, B, 0, num_pages, dtype, stream);
+}
+
+int gqa_decode_global_k_eq_v(const void* q, const void* v, const void* w_k,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t S_max,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!w_k) return GQA_ERR_NULL;
+  return run(GQA_GLOBAL, 0, false, q, nullptr, v, w_k, nullptr, 0, seq_lens, o, B, S_max, 0,
+             dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_global_k_eq_v_paged(const void* q, const void* v_pool, const void* w_k,
+                                   const int32_t* block_table, int32_t max_pages,
+                                   const int32_t* seq_lens, void* o, int32_t B,
+                                   int32_t num_pages, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!w_k) return GQA_ERR_NULL;
+  return run(GQA_GLOBAL, 0, true, q, nullptr, v_pool, w_k, block_table, max_pages, seq_lens, o,
+             B, 0, num_pages, dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_append_global_k_eq_v(const void* q_raw, const void* k_raw, const void* w_q,
+                             const void* w_k, const int32_t* seq_lens, void* q_out,
+                             void* v_cache, int32_t B, int32_t S_max, int32_t dtype,
+                             void* stream) {
+  return run_append(GQA_GLOBAL, false, true, q_raw, k_raw, nullptr, w_q, w_k, nullptr, 0,
+                    seq_lens, q_out, nullptr, v_cache, B, S_max, 0, dtype, stream);
+}
+
+int gqa_append_global_k_eq_v_paged(const void* q_raw, const void* k_raw, const void* w_q,
+                                   const void* w_k, const int32_t* block_table,
+                                   int32_t max_pages, const int32_t* seq_lens, void* q_out,
+                                   void* v_pool, int32_t B, int32_t num_pages, int32_t dtype,
+                                   void* stream) {
+  return run_append(GQA_GLOBAL, true, true, q_raw, k_raw, nullptr, w_q, w_k, block_table,
+                    max_pages, seq_lens, q_out, nullptr, v_pool, B, 0, num_pages, dtype, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity) {

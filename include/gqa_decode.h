@@ -167,6 +167,47 @@ int gqa_append_global_paged(const void* q_raw, const void* k_raw, const void* w_
                             const int32_t* seq_lens, void* q_out, void* k_pool, void* v_pool,
                             int32_t B, int32_t num_pages, int32_t dtype, void* stream);
 
+/* decodeGQA over a values-only cache (global layers).  On the global layers
+ * the values are the raw keys (the Model Spec page: "What to watch for" and
+ * attention_k_eq_v in "Published configuration"; the architecture page's
+ * compact forward pass takes V_raw = K_raw), so with u = K_raw / rms the
+ * cache's value row is u and the key row is rope(w_k * u, s).  These calls
+ * read only the value cache and rebuild each key in the kernel:
+ *   k_s = rope(w_k * v_s, s), s = the position of the row in its sequence,
+ * with the global RoPE of gqa_append_global (pairs (i, i+256), the first 64
+ * rotating by s * 1e6^(-2i/512)), then attend exactly as gqa_decode_global.
+ * That halves the bytes a decode step reads (4 KiB instead of 8 KiB per
+ * position in bf16).  Keys are rebuilt in fp32 (angles in double) and
+ * rounded to the dtype before the QK^T product, as a stored key would be;
+ * the query is multiplied by w_k (rounded to the dtype) on the 448
+ * coordinates that do not rotate.
+ * Arguments: q [B,32,512]; v [B,S_max,4,512] (contiguous) or v_pool
+ * [num_pages,16,4,512] with block_table [B,max_pages]; w_k [512] (the k_norm
+ * weight), all of one dtype; other arguments, the workspace (the size of
+ * gqa_decode_workspace_bytes(GQA_GLOBAL, ...)), the plan and errors are those
+ * of gqa_decode_global / gqa_decode_global_paged.  w_k NULL -> GQA_ERR_NULL. */
+int gqa_decode_global_k_eq_v(const void* q, const void* v, const void* w_k,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t S_max,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+int gqa_decode_global_k_eq_v_paged(const void* q, const void* v_pool, const void* w_k,
+                                   const int32_t* block_table, int32_t max_pages,
+                                   const int32_t* seq_lens, void* o, int32_t B,
+                                   int32_t num_pages, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+/* The append of the global layers for a values-only cache: as
+ * gqa_append_global (q_out and the value row u = k_raw / rms at pos) but no
+ * key row is stored. */
+int gqa_append_global_k_eq_v(const void* q_raw, const void* k_raw, const void* w_q,
+                             const void* w_k, const int32_t* seq_lens, void* q_out,
+                             void* v_cache, int32_t B, int32_t S_max, int32_t dtype,
+                             void* stream);
+int gqa_append_global_k_eq_v_paged(const void* q_raw, const void* k_raw, const void* w_q,
+                                   const void* w_k, const int32_t* block_table,
+                                   int32_t max_pages, const int32_t* seq_lens, void* q_out,
+                                   void* v_pool, int32_t B, int32_t num_pages, int32_t dtype,
+                                   void* stream);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:
@@ -210,7 +251,8 @@ int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
  * `capacity` launches are kept).  gqa_profile_read synchronises those events
  * and reports, per kernel kind, the number of launches and their summed
  * duration in milliseconds (kind 2*variant: main kernel of that variant,
- * 2*variant+1: its combine kernel, 4+variant: its append kernel); it also
+ * 2*variant+1: its combine kernel, 4+variant: its append kernel; the
+ * values-only global calls: 6 main, 7 combine, 8 append); it also
  * disables recording and releases
  * the events.  Measurement only: not thread-safe, not for captured graphs. */
 int gqa_profile_begin(int32_t capacity);

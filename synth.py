@@ -16,7 +16,9 @@ gemma-4-31B Model Spec page, "Compute-graph nodes" table):
     "rmsnormUnit"), i.e. unit RMS;
   * decodeGQA ("values = keys"): k and v come from the same raw draw r,
     v = unit-RMS(r), k = w_k * unit-RMS(r); RoPE is not applied (it is an
-    upstream node; the kernel sees post-RoPE keys whatever they are).
+    upstream node; the kernel sees post-RoPE keys whatever they are).  The
+    values-only calls take v and w_k (kept in ``Case.w_k``, rounded to the
+    dtype) and rebuild their own keys.
 Only positions inside the attended range [max(0, L-W), L) are drawn; every
 other cache slot (and every unreferenced page) holds ``fill``: NaN for
 correctness runs (so a stray read shows up), zero for timing runs.  Block-table
@@ -64,6 +66,7 @@ class Case:
     block_table: torch.Tensor | None  # [B, max_pages] int32 or None
     cap: int                 # S_max (contiguous) or max_pages*16 (paged)
     window: int
+    w_k: torch.Tensor | None = None  # [D] the k weight the keys were drawn with, in dtype
 
     @property
     def B(self):
@@ -177,7 +180,7 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
                 kr, vr = rows(b, L - lo)
                 k[b, lo:L] = kr.to(tdt)
                 v[b, lo:L] = vr.to(tdt)
-        return Case(variant, dtype, q, k, v, seq_lens.to(device), None, cap, W)
+        return Case(variant, dtype, q, k, v, seq_lens.to(device), None, cap, W, w_k.to(tdt))
 
     assert cap % PAGE == 0
     max_pages = cap // PAGE
@@ -214,7 +217,8 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
         idx = phys.to(device=device, dtype=torch.int64)
         k[idx] = kb.view(p1 - p0, PAGE, KV, D)
         v[idx] = vb.view(p1 - p0, PAGE, KV, D)
-    return Case(variant, dtype, q, k, v, seq_lens.to(device), bt.to(device), cap, W)
+    return Case(variant, dtype, q, k, v, seq_lens.to(device), bt.to(device), cap, W,
+                w_k.to(tdt))
 
 
 def make_workload(name: str, seed: int = 0, device="cpu", fill: float = float("nan"),

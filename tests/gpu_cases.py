@@ -57,11 +57,28 @@ def to_gpu(case: synth.Case) -> synth.Case:
     return synth.Case(case.variant, case.dtype, case.q.to(dev), case.k.to(dev), case.v.to(dev),
                       case.seq_lens.to(dev),
                       None if case.block_table is None else case.block_table.to(dev),
-                      case.cap, case.window)
+                      case.cap, case.window, None if case.w_k is None else case.w_k.to(dev))
 
 
 def to_cpu(case: synth.Case) -> synth.Case:
     return synth.Case(case.variant, case.dtype, case.q.cpu(), case.k.cpu(), case.v.cpu(),
                       case.seq_lens.cpu(),
                       None if case.block_table is None else case.block_table.cpu(),
-                      case.cap, case.window)
+                      case.cap, case.window, None if case.w_k is None else case.w_k.cpu())
+
+
+def hip_run_k_eq_v(case: synth.Case, workspace=None, stream=None, o=None) -> torch.Tensor:
+    """The values-only global call on the case's v and w_k (its k is not read)."""
+    if case.block_table is None:
+        return gqa.gqa_decode_global_k_eq_v(case.q, case.v, case.w_k, case.seq_lens, o=o,
+                                            workspace=workspace, stream=stream)
+    return gqa.gqa_decode_global_k_eq_v_paged(case.q, case.v, case.w_k, case.block_table,
+                                              case.seq_lens, o=o, workspace=workspace,
+                                              stream=stream)
+
+
+def oracle_run_k_eq_v(case: synth.Case, rows=None, nthreads=16) -> np.ndarray:
+    bt = None if case.block_table is None else synth.to_numpy(case.block_table)
+    return oracle.gqa_decode_k_from_v(synth.to_numpy(case.q), synth.to_numpy(case.v),
+                                      synth.to_numpy(case.w_k), synth.to_numpy(case.seq_lens),
+                                      block_table=bt, rows=rows, nthreads=nthreads)

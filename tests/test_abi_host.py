@@ -165,6 +165,29 @@ def test_append_arguments_fail_before_launch(lib):
     assert gl(ok, ok, ok, ok, ok, 8, ok, ok, ok, mis, 4, 8, 1, None) == -4
 
 
+def test_values_only_arguments_fail_before_launch(lib):
+    P = ctypes.c_void_p
+    ok, mis = P(0x10000), P(0x10008)
+    f, fp = lib.gqa_decode_global_k_eq_v, lib.gqa_decode_global_k_eq_v_paged
+    # f(q, v, w_k, seq_lens, o, B, S_max, dtype, ws, ws_bytes, stream)
+    assert f(ok, ok, None, ok, ok, 4, 64, 1, None, 0, None) == -1   # w_k is required
+    assert f(ok, None, ok, ok, ok, 4, 64, 1, None, 0, None) == -1
+    assert f(ok, ok, ok, ok, ok, 0, 64, 1, None, 0, None) == -2
+    assert f(ok, ok, ok, ok, ok, 4, 262145, 1, None, 0, None) == -2
+    assert f(ok, ok, ok, ok, ok, 4, 64, 5, None, 0, None) == -3
+    assert f(ok, ok, mis, ok, ok, 4, 64, 1, None, 0, None) == -4
+    assert f(ok, ok, ok, ok, ok, 4, 64, 1, None, 0, None) == -5     # stream plan needs workspace
+    # fp(q, v_pool, w_k, block_table, max_pages, seq_lens, o, B, num_pages, dtype, ws, ...)
+    assert fp(ok, ok, ok, None, 8, ok, ok, 4, 8, 1, None, 0, None) == -1
+    assert fp(ok, ok, ok, ok, 0, ok, ok, 4, 8, 1, None, 0, None) == -2
+    a, ap = lib.gqa_append_global_k_eq_v, lib.gqa_append_global_k_eq_v_paged
+    # a(q_raw, k_raw, w_q, w_k, seq_lens, q_out, v_cache, B, S_max, dtype, stream)
+    assert a(ok, ok, ok, ok, ok, ok, None, 4, 64, 1, None) == -1
+    assert a(ok, ok, ok, ok, ok, ok, ok, 0, 64, 1, None) == -2
+    assert a(ok, ok, ok, ok, ok, ok, mis, 4, 64, 1, None) == -4
+    assert ap(ok, ok, ok, ok, None, 8, ok, ok, ok, 4, 8, 1, None) == -1
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     q = torch.zeros(1, 32, 256, dtype=torch.bfloat16)
