@@ -226,6 +226,15 @@ struct RopeLds {
   double freq[kRopePairs];        // f_i = 1e6^(-2i/512)
 };
 
+// The per-wave LDS tile of the staged (bf16 keys-from-values) path: 16 rows of
+// 512 bf16 values, each row padded by one 16-byte chunk.
+template <bool KFV, bool BF16>
+constexpr bool kStaged = KFV && BF16;
+constexpr int kStageRow = 512 * 2 + 16;
+constexpr int kStageTileBytes = kTile * kStageRow;
+// followed by the rebuilt key chunks: 4 slots x 64 lanes x 16 bytes
+constexpr int kStageBytes = kStageTileBytes + 4 * 64 * 16;
+
 template <bool BF16>
 __device__ inline float elem_f32(const char* base, int i) {
   if constexpr (BF16) return bf16_value(*reinterpret_cast<const unsigned short*>(base + 2 * i));
@@ -266,9 +275,12 @@ __device__ inline void rope_base(RopeLds* rl, int wave, int pos0) {
 template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int g,
                                                  const SeqRange& sr, int k_begin, int k_end,
-                                                 int step, u32x4* myq, RopeLds* rl,
+                                                 int step, u32x4* myq, RopeLds* rl, char* stage,
                                                  WaveState<KV, D, BF16>& st) {
   static_assert(!KFV || (KV == 4 && D == 512), "keys from values: global layers only");
+  // bf16 keys from values: each tile is fetched once (key layout) and staged
+  // in the wave's LDS buffer, from which both operand layouts are read
+  constexpr bool STAGED = kStaged<KFV, BF16>;
   using Gm = Geo<KV, D, BF16>;
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
                 VBLK = Gm::VBLK, QPL = Gm::QPL;
@@ -388,11 +400,14 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     }
   };
 
-  // keys rebuilt from the value row in kreg: the lane's rotated pairs are
-  // chunks t < TA (coordinates < 64) and their partners t + TP (+256)
-  auto rebuild_keys = [&]() {
+  // Keys rebuilt from the value row in src: the lane's rotated pairs are
+  // chunks t < TA (coordinates < 64) and their partners t + TP (+256).  The
+  // result goes back into src, or (staged) to slots t and TA + t of the
+  // wave's LDS area of rotated chunks (slot-major, 16 bytes per lane).
+  constexpr int TA = kRopePairs / (4 * E), TP = 256 / (4 * E);
+  u32x4* rot = STAGED ? reinterpret_cast<u32x4*>(stage + kStageTileBytes) : nullptr;
+  auto rebuild_keys = [&](u32x4 (&src)[KCH]) {
     if constexpr (KFV) {
-      constexpr int TA = kRopePairs / (4 * E), TP = 256 / (4 * E);
       // position within the tile, opaque to the optimizer: the M entries are
       // loop-invariant and would otherwise be hoisted out of the tile loop
       // into 64 registers this kernel does not have
@@ -405,16 +420,16 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
         if constexpr (BF16) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            va[2 * q] = bf16_value(kreg[t][q] & 0xffffu);
-            va[2 * q + 1] = bf16_value(kreg[t][q] >> 16);
-            vb[2 * q] = bf16_value(kreg[t + TP][q] & 0xffffu);
-            vb[2 * q + 1] = bf16_value(kreg[t + TP][q] >> 16);
+            va[2 * q] = bf16_value(src[t][q] & 0xffffu);
+            va[2 * q + 1] = bf16_value(src[t][q] >> 16);
+            vb[2 * q] = bf16_value(src[t + TP][q] & 0xffffu);
+            vb[2 * q + 1] = bf16_value(src[t + TP][q] >> 16);
           }
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            va[e] = chunk_f32(kreg[t], e);
-            vb[e] = chunk_f32(kreg[t + TP], e);
+            va[e] = chunk_f32(src[t], e);
+            vb[e] = chunk_f32(src[t + TP], e);
           }
         }
         // four pairs at a time: the scheduler barrier bounds the LDS reads in
@@ -433,26 +448,44 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        u32x4 ka, kb;
         if constexpr (BF16) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            kreg[t][q] = bf16_bits(va[2 * q]) | (bf16_bits(va[2 * q + 1]) << 16);
-            kreg[t + TP][q] = bf16_bits(vb[2 * q]) | (bf16_bits(vb[2 * q + 1]) << 16);
+            ka[q] = bf16_bits(va[2 * q]) | (bf16_bits(va[2 * q + 1]) << 16);
+            kb[q] = bf16_bits(vb[2 * q]) | (bf16_bits(vb[2 * q + 1]) << 16);
           }
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            kreg[t][e] = __builtin_bit_cast(unsigned, va[e]);
-            kreg[t + TP][e] = __builtin_bit_cast(unsigned, vb[e]);
+            ka[e] = __builtin_bit_cast(unsigned, va[e]);
+            kb[e] = __builtin_bit_cast(unsigned, vb[e]);
           }
         }
+        if constexpr (STAGED) {
+          rot[t * 64 + lane] = ka;
+          rot[(TA + t) * 64 + lane] = kb;
+        } else {
+          src[t] = ka;
+          src[t + TP] = kb;
+        }
       }
+    }
+  };
+  // the QK^T operand chunk c of the lane (compile-time c)
+  auto key_op = [&](int c) -> u32x4 {
+    if constexpr (STAGED) {
+      if (c < TA) return rot[c * 64 + lane];
+      if (c >= TP && c < TP + TA) return rot[(TA + c - TP) * 64 + lane];
+      return *reinterpret_cast<const u32x4*>(stage + r * kStageRow + j * 16 + 64 * c);
+    } else {
+      return kreg[c];
     }
   };
 
   TileAt cur = tile_at(0);
   load_k(cur);
-  load_v(cur);
+  if constexpr (!STAGED) load_v(cur);
   if constexpr (KFV) rope_base(rl, threadIdx.x >> 6, cur.pos0);
 #pragma unroll
   for (int i = 0; i < QPL; ++i) {
@@ -467,7 +500,21 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     const bool more = it + 1 < n_it;
     const TileAt nxt = more ? tile_at(it + 1) : cur;
 
-    rebuild_keys();
+    if constexpr (STAGED) {
+      // stage the fetched tile (row r, chunks 4t+j: 16-byte lanes, rows
+      // padded by one chunk so the 16 rows of a lane group hit distinct
+      // banks), rebuild the rotated chunks from the registers, then refill
+      // the key registers with the next tile at once
+      char* srow = stage + r * kStageRow + j * 16;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) *reinterpret_cast<u32x4*>(srow + 64 * c) = kreg[c];
+      rebuild_keys(kreg);
+      if (more) load_k(nxt);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      rebuild_keys(kreg);
+    }
 
     // logits z[pos 4j+i][head r]
     f32x4 z;
@@ -478,9 +525,9 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
         for (int c = 0; c < KCH; c += 2) {
           const u32x4 q0 = r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
           const u32x4 q1 = r < G ? qrow[4 * c + 4 + j] : u32x4{0u, 0u, 0u, 0u};
-          z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c]),
+          z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c)),
                                                        __builtin_bit_cast(bf16x8, q0), z0, 0, 0, 0);
-          z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c + 1]),
+          z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c + 1)),
                                                        __builtin_bit_cast(bf16x8, q1), z1, 0, 0, 0);
         }
       } else {
@@ -498,8 +545,18 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       }
       z = z0 + z1;
     }
-    // the key registers are free: fetch the next tile's keys
-    if (more) load_k(nxt);
+    if constexpr (STAGED) {
+      // value operands: rows 4j+i (clamped as when fetched), chunks r+16*blk
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int blk = 0; blk < VBLK; ++blk)
+          vreg[i][blk] = *reinterpret_cast<const u32x4*>(stage + (4 * j + i) * kStageRow +
+                                                         (r + 16 * blk) * 16);
+    } else {
+      // the key registers are free: fetch the next tile's keys
+      if (more) load_k(nxt);
+    }
     if constexpr (KFV) {
       if (more) {
         // the base of the next tile (this tile's rebuilt keys no longer read it)
@@ -568,7 +625,9 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
                                                                   st.acc[blk][e], 0, 0, 0);
     }
     // the value registers are free: fetch the next tile's values
-    if (more) load_v(nxt);
+    if constexpr (!STAGED) {
+      if (more) load_v(nxt);
+    }
     if constexpr (PAGED) {
       if (it + 1 - it0 == 64) {
         it0 += 64;
@@ -647,6 +706,9 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ u32x4 s_q[kWaves][G * NCH];   // per-wave query heads of the current unit
   __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
   RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
+  constexpr bool STAGED = kStaged<KFV, BF16>;
+  __shared__ __attribute__((aligned(16))) char s_stage[STAGED ? kWaves * kStageBytes : 16];
+  char* stage = STAGED ? s_stage + (threadIdx.x >> 6) * kStageBytes : nullptr;
   if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
   if (threadIdx.x < 64) {
     int cnt[4];
@@ -717,7 +779,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
     const int k_begin = kk0;
     const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
     accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin, k_end, 1,
-                                               s_q[threadIdx.x >> 6], s_rope, st);
+                                               s_q[threadIdx.x >> 6], s_rope, stage, st);
 
     // the wave writes o when its slice holds the whole unit, else a partial
     if (r < G) {
@@ -753,7 +815,13 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, VBLK = Gm::VBLK;
   constexpr int LROW = D + 4;  // padded LDS row (floats)
   __shared__ u32x4 s_q[kWaves][G * NCH];
-  __shared__ float s_acc[(kWaves - 1) * G * LROW];
+  // the merge rows of waves 1..3; the staged path's per-wave tiles share the
+  // space (every wave has left its tile loop before the merge writes)
+  constexpr bool STAGED = kStaged<KFV, BF16>;
+  constexpr int ACC_BYTES = (kWaves - 1) * G * LROW * 4;
+  constexpr int POOL = STAGED && kWaves * kStageBytes > ACC_BYTES ? kWaves * kStageBytes : ACC_BYTES;
+  __shared__ __attribute__((aligned(16))) char s_pool[POOL];
+  float* s_acc = reinterpret_cast<float*>(s_pool);
   __shared__ float s_m[(kWaves - 1) * G];
   __shared__ float s_l[(kWaves - 1) * G];
   __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
@@ -780,7 +848,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
 
   WaveState<KV, D, BF16> st;
   accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, wave, sr.n, kWaves, s_q[wave], s_rope,
-                                            st);
+                                            STAGED ? s_pool + wave * kStageBytes : nullptr, st);
+  if constexpr (STAGED) __syncthreads();  // the tiles are dead before s_acc is written
 
   if (wave > 0 && r < G) {
     float* dst = s_acc + ((wave - 1) * G + r) * LROW;
