@@ -93,9 +93,10 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_traffic():
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3 --pmc
-    runs, valid only if taken on the current kernel source."""
+def read_traffic(key: str = "global_main"):
+    """HBM bytes per launch of a kernel (global_main: the dominant kernel) from
+    committed rocprofv3 --pmc runs, valid only if taken on the current kernel
+    source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -107,7 +108,7 @@ def read_traffic():
     if vals.get("source_sha256") != source_hash():
         return None
     try:
-        return float(vals["global_main_hbm_bytes_per_launch"])
+        return float(vals[f"{key}_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -368,6 +369,7 @@ def main():
         "v_GBps": round(kv_only / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(kv_only / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "speedup_vs_stored_keys": round(gl_ms / ms, 3) if ms else None,
+        "main_kernel_hbm_traffic": read_traffic("kfv_main"),
     }
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)

@@ -68,6 +68,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <bool BF16>
@@ -143,6 +144,13 @@ __device__ inline unsigned bf16_bits(float x) {
   return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
+// Two floats rounded to bf16 (RNE) and packed, the first in the low half: one
+// v_cvt_pk_bf16_f32.
+__device__ inline unsigned bf16_pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ inline float bf16_value(unsigned bits) {
   return __builtin_bit_cast(float, bits << 16);
 }
@@ -166,7 +174,7 @@ __device__ inline void store_run(char* dst, const float* v, int n) {
     for (int c = 0; c < n / 8; ++c) {
       u32x4 w;
       for (int q = 0; q < 4; ++q)
-        w[q] = bf16_bits(v[8 * c + 2 * q]) | (bf16_bits(v[8 * c + 2 * q + 1]) << 16);
+        w[q] = bf16_pack2(v[8 * c + 2 * q], v[8 * c + 2 * q + 1]);
       *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
     }
   } else {
@@ -327,7 +335,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
               const unsigned x = qstage[i][q], y = w[q];
               const float lo = bf16_value(x & 0xffffu) * bf16_value(y & 0xffffu);
               const float hi = bf16_value(x >> 16) * bf16_value(y >> 16);
-              qstage[i][q] = bf16_bits(lo) | (bf16_bits(hi) << 16);
+              qstage[i][q] = bf16_pack2(lo, hi);
             }
           } else {
 #pragma unroll
@@ -452,8 +460,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
         if constexpr (BF16) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            ka[q] = bf16_bits(va[2 * q]) | (bf16_bits(va[2 * q + 1]) << 16);
-            kb[q] = bf16_bits(vb[2 * q]) | (bf16_bits(vb[2 * q + 1]) << 16);
+            ka[q] = bf16_pack2(va[2 * q], va[2 * q + 1]);
+            kb[q] = bf16_pack2(vb[2 * q], vb[2 * q + 1]);
           }
         } else {
 #pragma unroll
@@ -595,12 +603,10 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
 
     if constexpr (BF16) {
-      unsigned pb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = bf16_bits(p[i]);
-      st.l += (bf16_value(pb[0]) + bf16_value(pb[1])) + (bf16_value(pb[2]) + bf16_value(pb[3]));
-      const s16x4 pt =
-          __builtin_bit_cast(s16x4, u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)});
+      const unsigned p01 = bf16_pack2(p[0], p[1]), p23 = bf16_pack2(p[2], p[3]);
+      st.l += (bf16_value(p01 & 0xffffu) + bf16_value(p01 >> 16)) +
+              (bf16_value(p23 & 0xffffu) + bf16_value(p23 >> 16));
+      const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
 #pragma unroll
       for (int blk = 0; blk < VBLK; ++blk) {
 #pragma unroll
@@ -659,7 +665,7 @@ __device__ __forceinline__ void store_o(const WaveState<KV, D, BF16>& st, char* 
         u32x4 w;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          w[q] = bf16_bits(st.acc[blk][2 * q][i] * inv) | (bf16_bits(st.acc[blk][2 * q + 1][i] * inv) << 16);
+          w[q] = bf16_pack2(st.acc[blk][2 * q][i] * inv, st.acc[blk][2 * q + 1][i] * inv);
         *reinterpret_cast<u32x4*>(dst + 16 * i) = w;
       } else {
         *reinterpret_cast<f32x4*>(dst + 16 * i) =
@@ -974,8 +980,8 @@ __global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
     for (int c = 0; c < 4; ++c) run[c] = Lt > 0.f ? A[c] * inv : 0.f;
   }
   if constexpr (BF16) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{bf16_bits(run[0]) | (bf16_bits(run[1]) << 16),
-                                           bf16_bits(run[2]) | (bf16_bits(run[3]) << 16)};
+    *reinterpret_cast<u32x2*>(dst) = u32x2{bf16_pack2(run[0], run[1]),
+                                           bf16_pack2(run[2], run[3])};
   } else {
     *reinterpret_cast<f32x4*>(dst) = f32x4{run[0], run[1], run[2], run[3]};
   }
@@ -1042,8 +1048,8 @@ __device__ inline void store_elems(char* p, const float (&x)[N]) {
 #pragma unroll
     for (int c = 0; c < N / 4; ++c)
       *reinterpret_cast<u32x2*>(p + 8 * c) =
-          u32x2{bf16_bits(x[4 * c]) | (bf16_bits(x[4 * c + 1]) << 16),
-                bf16_bits(x[4 * c + 2]) | (bf16_bits(x[4 * c + 3]) << 16)};
+          u32x2{bf16_pack2(x[4 * c], x[4 * c + 1]),
+                bf16_pack2(x[4 * c + 2], x[4 * c + 3])};
   } else {
 #pragma unroll
     for (int c = 0; c < N / 4; ++c)
