@@ -70,6 +70,10 @@ def load(path: str = LIBRARY):
     kv = lib.oracle_gqa_decode_k_from_v
     kv.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, p, i32, p, i32]
     kv.restype = ctypes.c_int
+    pf = lib.oracle_gqa_prefill
+    pf.argtypes = [ctypes.c_int, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, i32, p,
+                   i32, p, i32]
+    pf.restype = ctypes.c_int
     ap = lib.oracle_gqa_append_rows
     ap.argtypes = [ctypes.c_int, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
     ap.restype = ctypes.c_int
@@ -217,3 +221,54 @@ def gqa_decode_k_from_v(q, v, w_k, seq_lens, block_table=None, num_pages=None, r
     if rc != 0:
         raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
     return out.reshape(B, HEADS, 512) if rows is None else out
+
+
+def gqa_prefill(variant, q, k, v, cu_q, seq_lens, block_table=None, num_pages=None, rows=None,
+                nthreads: int | None = None, window: int | None = None, lib=None) -> np.ndarray:
+    """Reference prefill attention in fp64: query row n of sequence b (cu_q[b] <= n
+    < cu_q[b+1]) sits at position seq_lens[b] - T_b + (n - cu_q[b]) and attends
+    to the keys at positions p - W < s <= p (sliding) or s <= p (global).
+
+    q [N,32,D]; cu_q [B+1] int32; k, v and block_table as gqa_decode.  rows:
+    optional list of (query row, head) pairs.  Returns [N,32,D] or [len(rows), D].
+    """
+    KV, D, W = VARIANTS[variant] if isinstance(variant, str) else variant
+    if window is not None:
+        W = window
+    lib = lib or load()
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share a dtype")
+    cu_q = np.ascontiguousarray(cu_q, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = seq_lens.shape[0]
+    N = q.shape[0]
+    if q.shape != (N, HEADS, D) or cu_q.shape != (B + 1,):
+        raise ValueError("q must be [N,32,D] and cu_q [B+1]")
+    if block_table is None:
+        if k.ndim != 4 or k.shape[0] != B or k.shape[2:] != (KV, D) or v.shape != k.shape:
+            raise ValueError("contiguous k/v must be [B,S,KV,D]")
+        cap, max_pages, n_pages, bt = k.shape[1], 0, 0, None
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B,max_pages]")
+        if k.ndim != 4 or k.shape[1:] != (PAGE, KV, D) or v.shape != k.shape:
+            raise ValueError("paged k/v must be [num_pages,16,KV,D]")
+        max_pages = bt.shape[1]
+        n_pages = k.shape[0] if num_pages is None else num_pages
+        cap = max_pages * PAGE
+    if rows is None:
+        rows_arr, n_rows = None, N * HEADS
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, D), dtype=np.float64)
+    nthreads = nthreads or min(os.cpu_count() or 1, 16)
+    rc = lib.oracle_gqa_prefill(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(seq_lens),
+                                _ptr(bt), B, N, cap, max_pages, n_pages, KV, D, W, _ptr(rows_arr),
+                                n_rows, _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
+    return out.reshape(N, HEADS, D) if rows is None else out

@@ -60,8 +60,10 @@ typedef struct {
   const int32_t *block_table; /* NULL: contiguous cache */
   int32_t B, cap, max_pages, num_pages, KV, D, window;
   const void *w_k;     /* non-NULL: keys rebuilt from values (global layers) */
-  const int32_t *rows; /* (b, h) pairs or NULL for every row */
+  const int32_t *rows; /* (b, h) pairs -- prefill: (token row, h) -- or NULL for every row */
   int32_t n_rows;
+  const int32_t *cu_q; /* non-NULL: prefill, query rows cu_q[b] .. cu_q[b+1]-1 of sequence b */
+  int32_t N;           /* prefill: query rows */
   double *out;
   /* shared work counter and first error */
   int32_t next;
@@ -149,6 +151,57 @@ static int orc_one_row(const orc_job *j, int b, int h, double *out) {
   return ORC_OK;
 }
 
+/* Prefill: output row o[n,h,:] of query row n (a token of a chunk appended to
+ * the cache just before attention; "Prefill, Cache, and Long Context" and
+ * the compact forward pass of the architecture page).  Token t of the T_b
+ * tokens of sequence b sits at position p = seq_lens[b] - T_b + t
+ * (positions = past_seen_tokens + arange(T_current), past_seen = L - T) and
+ * attends to the keys the masks keep: full mask s <= p, sliding mask
+ * p - W < s <= p.  The rest is the decode definition above. */
+static int orc_prefill_row(const orc_job *j, int n, int h, double *out) {
+  const int D = j->D;
+  const int kvh = h / (ORC_HEADS / j->KV); /* kv head of query head h */
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  int b = 0; /* the sequence owning query row n */
+  while (b < j->B && j->cu_q[b + 1] <= n) ++b;
+  if (b >= j->B) return ORC_ERR_ARG;
+  const int64_t T_b = j->cu_q[b + 1] - j->cu_q[b];
+  const int64_t Lb = j->seq_lens[b];
+  if (Lb > j->cap) return ORC_ERR_SEQLEN;
+  const int64_t pos = Lb - T_b + (n - j->cu_q[b]);
+  if (pos < 0) return ORC_OK; /* chunk longer than the sequence: outside the domain */
+  /* keys kept by the mask: full s <= pos; sliding pos - W < s <= pos */
+  const int64_t first = (j->window > 0 && pos - j->window + 1 > 0) ? pos - j->window + 1 : 0;
+  const int64_t count = pos - first + 1;
+
+  double *score = (double *)malloc((size_t)count * sizeof(double));
+  if (!score) return ORC_ERR_NOMEM;
+  const size_t q_at = ((size_t)n * ORC_HEADS + h) * (size_t)D;
+  for (int64_t s = first; s <= pos; ++s) {
+    const int64_t at = orc_row_offset(j, b, s, kvh);
+    if (at < 0) { free(score); return ORC_ERR_PAGE; }
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += orc_elem(j->q, j->dtype, q_at + d) * orc_elem(j->k, j->dtype, (size_t)at + d);
+    score[s - first] = dot; /* scale 1 */
+  }
+  double top = -INFINITY;
+  for (int64_t i = 0; i < count; ++i) top = score[i] > top ? score[i] : top;
+  double total = 0.0;
+  for (int64_t i = 0; i < count; ++i) {
+    score[i] = exp(score[i] - top);
+    total += score[i];
+  }
+  for (int64_t s = first; s <= pos; ++s) {
+    const int64_t at = orc_row_offset(j, b, s, kvh);
+    for (int d = 0; d < D; ++d)
+      out[d] += score[s - first] * orc_elem(j->v, j->dtype, (size_t)at + d);
+  }
+  for (int d = 0; d < D; ++d) out[d] = out[d] / total;
+  free(score);
+  return ORC_OK;
+}
+
 static void *orc_worker(void *arg) {
   orc_job *j = (orc_job *)arg;
   for (;;) {
@@ -165,9 +218,15 @@ static void *orc_worker(void *arg) {
       b = r / ORC_HEADS;
       h = r % ORC_HEADS;
     }
-    int rc = (b < 0 || b >= j->B || h < 0 || h >= ORC_HEADS)
-                 ? ORC_ERR_ARG
-                 : orc_one_row(j, b, h, j->out + (size_t)r * j->D);
+    int rc;
+    if (j->cu_q) /* (b, h) is (query row, head) */
+      rc = (b < 0 || b >= j->N || h < 0 || h >= ORC_HEADS)
+               ? ORC_ERR_ARG
+               : orc_prefill_row(j, b, h, j->out + (size_t)r * j->D);
+    else
+      rc = (b < 0 || b >= j->B || h < 0 || h >= ORC_HEADS)
+               ? ORC_ERR_ARG
+               : orc_one_row(j, b, h, j->out + (size_t)r * j->D);
     if (rc) {
       pthread_mutex_lock(&j->mu);
       if (!j->err) j->err = rc;
@@ -192,18 +251,23 @@ static void *orc_worker(void *arg) {
  *   nthreads     worker threads (>= 1)
  * Returns 0 or a negative ORC_ERR_* code.
  */
-static int orc_decode(int dtype, const void *q, const void *k, const void *v, const void *w_k,
-                      const int32_t *seq_lens, const int32_t *block_table, int32_t B,
-                      int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV, int32_t D,
-                      int32_t window, const int32_t *rows, int32_t n_rows, double *out,
-                      int32_t nthreads) {
+static int orc_run(int dtype, const void *q, const void *k, const void *v, const void *w_k,
+                   const int32_t *cu_q, int32_t N, const int32_t *seq_lens,
+                   const int32_t *block_table, int32_t B, int32_t cap, int32_t max_pages,
+                   int32_t num_pages, int32_t KV, int32_t D, int32_t window,
+                   const int32_t *rows, int32_t n_rows, double *out, int32_t nthreads) {
   if (!q || !(k || w_k) || !v || !seq_lens || !out) return ORC_ERR_ARG;
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
   if (B < 1 || cap < 1 || KV < 1 || ORC_HEADS % KV != 0 || D < 1) return ORC_ERR_ARG;
   if (w_k && !(KV == 4 && D == 512)) return ORC_ERR_ARG;
   if (block_table && (max_pages < 1 || num_pages < 1 || cap != max_pages * ORC_PAGE))
     return ORC_ERR_ARG;
-  if (!rows) n_rows = B * ORC_HEADS;
+  if (cu_q) {
+    if (N < 0 || cu_q[0] != 0 || cu_q[B] != N) return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+      if (cu_q[b + 1] < cu_q[b]) return ORC_ERR_ARG;
+  }
+  if (!rows) n_rows = (cu_q ? N : B) * ORC_HEADS;
   if (n_rows < 0) return ORC_ERR_ARG;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
@@ -215,6 +279,7 @@ static int orc_decode(int dtype, const void *q, const void *k, const void *v, co
   j.B = B; j.cap = cap; j.max_pages = max_pages; j.num_pages = num_pages;
   j.KV = KV; j.D = D; j.window = window;
   j.rows = rows; j.n_rows = n_rows; j.out = out;
+  j.cu_q = cu_q; j.N = N;
   pthread_mutex_init(&j.mu, NULL);
 
   pthread_t th[256];
@@ -247,8 +312,8 @@ int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
                       int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV,
                       int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
                       double *out, int32_t nthreads) {
-  return orc_decode(dtype, q, k, v, NULL, seq_lens, block_table, B, cap, max_pages, num_pages,
-                    KV, D, window, rows, n_rows, out, nthreads);
+  return orc_run(dtype, q, k, v, NULL, NULL, 0, seq_lens, block_table, B, cap, max_pages,
+                 num_pages, KV, D, window, rows, n_rows, out, nthreads);
 }
 
 /*
@@ -266,8 +331,33 @@ int oracle_gqa_decode_k_from_v(int dtype, const void *q, const void *v, const vo
                                const int32_t *rows, int32_t n_rows, double *out,
                                int32_t nthreads) {
   if (!w_k) return ORC_ERR_ARG;
-  return orc_decode(dtype, q, NULL, v, w_k, seq_lens, block_table, B, cap, max_pages, num_pages,
-                    4, 512, 0, rows, n_rows, out, nthreads);
+  return orc_run(dtype, q, NULL, v, w_k, NULL, 0, seq_lens, block_table, B, cap, max_pages,
+                 num_pages, 4, 512, 0, rows, n_rows, out, nthreads);
+}
+
+/*
+ * oracle_gqa_prefill -- attention of a chunk of new tokens per sequence
+ * (prefill / chunked prefill: "Prefill, Cache, and Long Context" on the
+ * architecture page; the masks of its compact forward pass).  The chunk's K/V
+ * rows are already in the cache: sequence b holds seq_lens[b] positions, the
+ * last T_b = cu_q[b+1] - cu_q[b] of which are its query tokens.
+ *   q        [N, 32, D], query rows of sequence b at cu_q[b] .. cu_q[b+1]-1
+ *   cu_q     [B+1] int32, cu_q[0] = 0, non-decreasing, cu_q[B] = N
+ *   k, v, seq_lens, block_table, cap, max_pages, num_pages, KV, D, window:
+ *            as oracle_gqa_decode (window <= 0: full causal mask)
+ *   rows     n_rows (query row, head) pairs, or NULL for all N*32 rows
+ *   out      [n_rows, D] doubles
+ * A token whose position would be negative (T_b > seq_lens[b]) gets a zero row.
+ */
+int oracle_gqa_prefill(int dtype, const void *q, const void *k, const void *v,
+                       const int32_t *cu_q, const int32_t *seq_lens,
+                       const int32_t *block_table, int32_t B, int32_t N, int32_t cap,
+                       int32_t max_pages, int32_t num_pages, int32_t KV, int32_t D,
+                       int32_t window, const int32_t *rows, int32_t n_rows, double *out,
+                       int32_t nthreads) {
+  if (!cu_q || !k) return ORC_ERR_ARG;
+  return orc_run(dtype, q, k, v, NULL, cu_q, N, seq_lens, block_table, B, cap, max_pages,
+                 num_pages, KV, D, window, rows, n_rows, out, nthreads);
 }
 
 /*

@@ -132,14 +132,15 @@ def draw_seq_lens(lens, B: int, seed: int) -> torch.Tensor:
 
 def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool = False,
               seed: int = 0, device="cpu", fill: float = float("nan"), window: int | None = None,
-              extra_pages: int = 0, alloc_all_pages: bool = False) -> Case:
+              extra_pages: int = 0, alloc_all_pages: bool = False, draw_from=None) -> Case:
     """Build one seeded case.
 
     seq_lens: int list/tensor [B] (values outside [0, cap] are the caller's
     business).  paged: lay K/V out as a page pool with a random page
     permutation; the pool holds exactly the pages the attended ranges touch
     (all pages below L when ``alloc_all_pages``) plus ``extra_pages``
-    unreferenced ones.  window: override of the variant's window.
+    unreferenced ones.  window: override of the variant's window.  draw_from:
+    optional per-sequence first position to draw (instead of L - window).
     """
     KV, D, W = VARIANTS[variant]
     if window is not None:
@@ -170,6 +171,8 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
     for b in range(B):
         L = max(0, min(int(seq_lens[b]), cap))
         lo = max(0, L - W) if W > 0 else 0
+        if draw_from is not None:
+            lo = max(0, min(int(draw_from[b]), L))
         ranges.append((lo, L))
 
     if not paged:
@@ -221,6 +224,87 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
                 w_k.to(tdt))
 
 
+@dataclasses.dataclass
+class PrefillCase:
+    """A chunk of T_b new tokens per sequence, already appended to the cache:
+    sequence b holds seq_lens[b] positions, its query rows cu_q[b] .. cu_q[b+1]-1
+    are its last T_b positions."""
+    variant: str
+    dtype: str
+    q: torch.Tensor          # [N, 32, D]
+    k: torch.Tensor          # as Case
+    v: torch.Tensor
+    cu_q: torch.Tensor       # [B+1] int32
+    seq_lens: torch.Tensor   # [B] int32
+    block_table: torch.Tensor | None
+    cap: int
+    window: int
+
+    @property
+    def B(self):
+        return self.seq_lens.shape[0]
+
+    @property
+    def N(self):
+        return self.q.shape[0]
+
+    @property
+    def KV(self):
+        return VARIANTS[self.variant][0]
+
+    @property
+    def D(self):
+        return VARIANTS[self.variant][1]
+
+    def attended_pairs(self) -> int:
+        """Unmasked (query token, key) pairs of one kv head and one query head."""
+        n = 0
+        lens = self.seq_lens.tolist()
+        cu = self.cu_q.tolist()
+        for b, L in enumerate(lens):
+            T = cu[b + 1] - cu[b]
+            for t in range(T):
+                p = L - T + t
+                if p < 0:
+                    continue
+                n += p + 1 - (max(0, p - self.window + 1) if self.window > 0 else 0)
+        return n
+
+    def flops(self) -> int:
+        """Algorithmic flops: QK^T and PV over every unmasked pair, all 32 heads."""
+        return 4 * HEADS * self.D * self.attended_pairs()
+
+
+def make_prefill_case(variant: str, dtype: str, cap: int, seq_lens, q_lens, paged: bool = False,
+                      seed: int = 0, device="cpu", fill: float = float("nan"),
+                      window: int | None = None, extra_pages: int = 0) -> PrefillCase:
+    """Seeded prefill case: the cache rows every query of the chunk attends to are
+    drawn like make_case's (positions from the first chunk token's window start
+    to seq_lens[b]); every other slot holds ``fill``.  q [N,32,D] is drawn like
+    the decode queries (per-head RMS-normalised times w_q)."""
+    KV, D, W = VARIANTS[variant]
+    if window is not None:
+        W = window
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int32).cpu()
+    q_lens = torch.as_tensor(q_lens, dtype=torch.int32).cpu()
+    B = seq_lens.shape[0]
+    draw_from = []
+    for b in range(B):
+        p0 = int(seq_lens[b]) - int(q_lens[b])  # position of the first chunk token
+        draw_from.append(max(0, p0 - W + 1) if W > 0 else 0)
+    c = make_case(variant, dtype, B, cap, seq_lens, paged=paged, seed=seed, device=device,
+                  fill=fill, window=W, extra_pages=extra_pages, draw_from=draw_from)
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(q_lens, 0)
+    N = int(cu[-1])
+    g_w = _gen(seed, 5, device)
+    w_q = torch.empty(D, device=device).uniform_(0.2, 0.4, generator=g_w)
+    g_q = _gen(seed, 6, device)
+    q = (w_q * rms_unit(torch.randn(N, HEADS, D, generator=g_q, device=device)))
+    return PrefillCase(variant, dtype, q.to(TORCH_DTYPES[dtype]), c.k, c.v, cu.to(device),
+                       c.seq_lens, c.block_table, cap, W)
+
+
 def make_workload(name: str, seed: int = 0, device="cpu", fill: float = float("nan"),
                   B: int | None = None, window: int | None = None) -> Case:
     """One of WORKLOADS by name (B may be cut down for a quick CPU-sized run; `window`
@@ -251,7 +335,7 @@ def expected_kv_bytes(name: str) -> float:
     return w["B"] * n * KV * D * 2 * eb
 
 
-__all__ = ["Case", "make_case", "make_workload", "WORKLOADS", "VARIANTS", "to_numpy",
+__all__ = ["Case", "make_case", "make_workload", "PrefillCase", "make_prefill_case", "WORKLOADS", "VARIANTS", "to_numpy",
            "draw_seq_lens", "rms_unit", "expected_kv_bytes", "HEADS", "PAGE"]
 
 if __name__ == "__main__":  # pragma: no cover - quick look at the workloads
