@@ -23,7 +23,8 @@ EXPORTED_SYMBOLS = (
     "gqa_decode_sliding_window_plan", "gqa_append_sliding", "gqa_append_sliding_paged",
     "gqa_append_global", "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
     "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
-    "gqa_append_global_k_eq_v_paged",
+    "gqa_append_global_k_eq_v_paged", "gqa_prefill_sliding", "gqa_prefill_global",
+    "gqa_prefill_sliding_paged", "gqa_prefill_global_paged",
 )
 
 
@@ -70,6 +71,12 @@ def library():
                                                    p]
     lib.gqa_append_global_k_eq_v.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p]
     lib.gqa_append_global_k_eq_v_paged.argtypes = [p, p, p, p, p, i32, p, p, p, i32, i32, i32, p]
+    for name in ("gqa_prefill_sliding", "gqa_prefill_global"):
+        getattr(lib, name).argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, p]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("gqa_prefill_sliding_paged", "gqa_prefill_global_paged"):
+        getattr(lib, name).argtypes = [p, p, p, p, i32, p, p, p, i32, i32, i32, i32, p]
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("gqa_append_sliding", "gqa_append_sliding_paged", "gqa_append_global",
                  "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
                  "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
@@ -152,7 +159,7 @@ def profile_read() -> dict:
     """{(variant, kernel): (launches, total_ms)} for variant in sliding / global /
     global_k_eq_v (global layers over a values-only cache) and kernel in
     main/combine/append."""
-    n = 9
+    n = 11
     counts = (ctypes.c_int32 * n)()
     ms = (ctypes.c_double * n)()
     rc = library().gqa_profile_read(counts, ms, n)
@@ -164,6 +171,8 @@ def profile_read() -> dict:
             out[(vname, kname)] = (counts[kind], ms[kind])
     for kind, kname in ((6, "main"), (7, "combine"), (8, "append")):
         out[("global_k_eq_v", kname)] = (counts[kind], ms[kind])
+    for vi, vname in enumerate(("sliding", "global")):
+        out[(vname, "prefill")] = (counts[9 + vi], ms[9 + vi])
     return out
 
 
@@ -462,3 +471,58 @@ def gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache, block_ta
     if rc:
         raise GqaError(name, rc)
     return q_out
+
+
+def _prefill_call(variant, q, k, v, cu_q, seq_lens, block_table, o, stream):
+    KV = 16 if variant == GQA_SLIDING else 4
+    D = 256 if variant == GQA_SLIDING else 512
+    if q.dim() != 3 or q.shape[1:] != (HEADS, D):
+        raise ValueError(f"q must be [N,32,{D}]")
+    B = seq_lens.shape[0]
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
+        raise ValueError("seq_lens must be int32 [B]")
+    if cu_q.dtype != torch.int32 or cu_q.shape != (B + 1,):
+        raise ValueError("cu_q must be int32 [B+1]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    N = q.shape[0]
+    lib = library()
+    st = _stream(stream, q.device)
+    kind = "sliding" if variant == GQA_SLIDING else "global"
+    if block_table is None:
+        if k.dim() != 4 or k.shape[0] != B or k.shape[2:] != (KV, D) or v.shape != k.shape:
+            raise ValueError(f"k/v must be [B,S_max,{KV},{D}]")
+        name = f"gqa_prefill_{kind}"
+        rc = getattr(lib, name)(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_q, "cu_q"),
+                                _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N, k.shape[1],
+                                _dtype_code(q), st)
+    else:
+        if k.dim() != 4 or k.shape[1:] != (PAGE, KV, D) or v.shape != k.shape:
+            raise ValueError(f"k_pool/v_pool must be [num_pages,16,{KV},{D}]")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B,max_pages]")
+        name = f"gqa_prefill_{kind}_paged"
+        rc = getattr(lib, name)(_dev(q, "q"), _dev(k, "k_pool"), _dev(v, "v_pool"),
+                                _dev(block_table, "block_table"), block_table.shape[1],
+                                _dev(cu_q, "cu_q"), _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N,
+                                k.shape[0], _dtype_code(q), st)
+    if rc:
+        raise GqaError(name, rc)
+    return o
+
+
+def gqa_prefill_sliding(q, k, v, cu_q, seq_lens, block_table=None, o=None, stream=None):
+    """Prefill of the sliding layers: query rows q [N,32,256] of the last
+    cu_q[b+1]-cu_q[b] positions of each sequence, causal within the 1024-window;
+    the cache (contiguous, or paged with block_table) already holds the chunk."""
+    return _prefill_call(GQA_SLIDING, q, k, v, cu_q, seq_lens, block_table, o, stream)
+
+
+def gqa_prefill_global(q, k, v, cu_q, seq_lens, block_table=None, o=None, stream=None):
+    """Prefill of the global layers (q [N,32,512], full causal mask)."""
+    return _prefill_call(GQA_GLOBAL, q, k, v, cu_q, seq_lens, block_table, o, stream)

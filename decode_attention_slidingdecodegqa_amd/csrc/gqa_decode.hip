@@ -1155,6 +1155,298 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
   }
 }
 
+// ----------------------------------------------------------------- prefill
+// Attention of a chunk of new tokens per sequence (prefill / chunked prefill),
+// the chunk's K/V rows already in the cache: query row n of sequence b
+// (cu_q[b] <= n < cu_q[b+1], T_b rows) sits at position p = L_b - T_b + t and
+// attends to the keys its mask keeps (global: s <= p; sliding: p - W < s <= p).
+//
+// Work: the query rows of one (sequence, kv head g) form T_b*G columns
+// (token-major, the G heads of a token adjacent); a wave takes 16 of them and
+// runs the decode tile loop over the union of their key ranges with all 16
+// MFMA columns in use, each column masked to its own range.  A work-group's
+// four waves take consecutive column blocks of the same (b, g), so they read
+// the same K/V tiles close together in time.
+
+struct PrefillArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  char* o;
+  int32_t B, N, cap, max_pages, num_pages, window;
+};
+
+constexpr int kPrefillCols = 16;                  // query columns per wave
+constexpr int kPrefillColsPerWg = kPrefillCols * kWaves;
+
+template <int KV, bool BF16>
+constexpr int prefill_waves_per_simd() {
+  return KV == 16 ? 2 : 1;
+}
+
+template <int KV, int D, bool PAGED, bool BF16>
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) void gqa_prefill_kernel(
+    PrefillArgs a) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
+                VBLK = Gm::VBLK;
+  constexpr size_t POS = Gm::POS;
+  constexpr int QPL = kPrefillCols * NCH / 64;  // query chunks per lane when staging
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int g = blockIdx.y;
+
+  // ---- work-groups per sequence (ceil(T_b*G / 64)) and their prefix, in LDS
+  __shared__ int s_wg0[kMaxBatch + 1];
+  __shared__ int s_cu[kMaxBatch + 1];
+  __shared__ int s_len[kMaxBatch];
+  __shared__ u32x4 s_q[kWaves][kPrefillCols * NCH];
+  if (threadIdx.x < 64) {
+    int cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      cnt[i] = 0;
+      if (b < a.B) {
+        const int c0 = a.cu_q[b], c1 = a.cu_q[b + 1];
+        const int T = c1 > c0 ? c1 - c0 : 0;
+        cnt[i] = (T * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg;
+        s_cu[b] = c0;
+        s_len[b] = a.seq_lens[b];
+        if (b == a.B - 1) s_cu[a.B] = c1;
+      }
+    }
+    const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    int incl = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int run_b = incl - lsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      if (b < a.B) s_wg0[b] = run_b;
+      run_b += cnt[i];
+    }
+    if (lane == 63) s_wg0[a.B] = incl;
+  }
+  __syncthreads();  // the only barrier: waves may leave below
+  const int wg = blockIdx.x;
+  if (wg >= s_wg0[a.B]) return;
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = a.B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (s_wg0[mid] <= wg) lo_b = mid;
+      else hi_b = mid - 1;
+    }
+    b = lo_b;
+  }
+  const int cu = s_cu[b];
+  const int T = s_cu[b + 1] - cu;
+  const int cols = T * G;
+  const int col0 = ((wg - s_wg0[b]) * kWaves + wave) * kPrefillCols;
+  if (col0 >= cols) return;
+  const int L = min(s_len[b], a.cap);  // clamped for memory safety
+
+  // ---- this lane's column (n = r): token, head, position, key range
+  const int col = col0 + r;
+  const bool live = col < cols;
+  const int t_n = (live ? col : cols - 1) / G;
+  const int head = g * G + (live ? col : cols - 1) % G;
+  const int p_n = L - T + t_n;
+  const int lo_n = a.window > 0 ? max(0, p_n - a.window + 1) : 0;
+  // the wave's key range: the union over its columns (token-major: first and last)
+  const int t_first = col0 / G;
+  const int t_last = (min(col0 + kPrefillCols, cols) - 1) / G;
+  const int p_last = L - T + t_last;
+  const int p_first = max(L - T + t_first, 0);
+  const int range_lo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
+  const int range_hi = p_last;  // inclusive
+  char* o_row = a.o + ((size_t)(cu + t_n) * kHeads + head) * ROW;
+
+  WaveState<KV, D, BF16> st;
+#pragma unroll
+  for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  if (range_hi >= 0) {
+    // ---- stage the 16 columns' query rows in the wave's LDS slice
+    u32x4* myq = s_q[wave];
+    {
+      u32x4 qs[QPL];
+#pragma unroll
+      for (int i = 0; i < QPL; ++i) {
+        const int c = lane + 64 * i;     // chunk c of the slice: column c / NCH
+        const int cn = col0 + c / NCH;
+        const int cc = min(cn, cols - 1);
+        const char* src = a.q + ((size_t)(cu + cc / G) * kHeads + g * G + cc % G) * ROW;
+        qs[i] = cn < cols ? load16(src + (size_t)(c % NCH) * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < QPL; ++i) myq[lane + 64 * i] = qs[i];
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    const u32x4* qrow = myq + r * NCH;
+    const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+
+    struct TileAt {
+      const char* kb;
+      const char* vb;
+      int pos0;
+      bool ok;
+    };
+    auto tile_at = [&](int tile) {
+      TileAt ta;
+      ta.pos0 = tile * kTile;
+      size_t off;
+      if constexpr (PAGED) {
+        const int page = bt[tile];
+        ta.ok = page >= 0 && page < a.num_pages;
+        off = ((size_t)(ta.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+      } else {
+        ta.ok = true;
+        off = (((size_t)b * a.cap + ta.pos0) * KV + g) * (size_t)ROW;
+      }
+      ta.kb = a.k + off;
+      ta.vb = a.v + off;
+      return ta;
+    };
+    auto clamp_row = [&](int pos0, int row) {
+      const int p = min(max(pos0 + row, range_lo), range_hi);
+      return p - pos0;
+    };
+    u32x4 kreg[KCH];
+    u32x4 vreg[4][VBLK];
+    auto load_k = [&](const TileAt& ta) {
+      const char* rowp = ta.kb + (size_t)clamp_row(ta.pos0, r) * POS;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) kreg[c] = load16(rowp + (4 * c + j) * 16);
+    };
+    auto load_v = [&](const TileAt& ta) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* rowp = ta.vb + (size_t)clamp_row(ta.pos0, 4 * j + i) * POS;
+#pragma unroll
+        for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16(rowp + (r + 16 * blk) * 16);
+      }
+    };
+
+    const int tile_begin = range_lo / kTile, tile_end = range_hi / kTile;  // inclusive
+    TileAt cur = tile_at(tile_begin);
+    load_k(cur);
+    load_v(cur);
+    for (int tile = tile_begin; tile <= tile_end; ++tile) {
+      const bool more = tile < tile_end;
+      const TileAt nxt = more ? tile_at(tile + 1) : cur;
+      // logits z[key 4j+i][column r]
+      f32x4 z;
+      {
+        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF16) {
+#pragma unroll
+          for (int c = 0; c < KCH; c += 2) {
+            z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c]),
+                                                         __builtin_bit_cast(bf16x8, qrow[4 * c + j]),
+                                                         z0, 0, 0, 0);
+            z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kreg[c + 1]),
+                __builtin_bit_cast(bf16x8, qrow[4 * c + 4 + j]), z1, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) {
+            const u32x4 qc = qrow[4 * c + j];
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e), chunk_f32(qc, e),
+                                                        z0, 0, 0, 0);
+              z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e + 1),
+                                                        chunk_f32(qc, e + 1), z1, 0, 0, 0);
+            }
+          }
+        }
+        z = z0 + z1;
+      }
+      if (more) load_k(nxt);
+      // each column keeps the keys of its own mask
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = cur.pos0 + 4 * j + i;
+        if (!(cur.ok && live && s >= lo_n && s <= p_n)) z[i] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool grow = tmax > st.m + kRescaleGap;
+      if (__any(grow)) {
+        const float m_next = grow ? tmax : st.m;
+        const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+        if (grow) {
+          st.l *= alpha;
+#pragma unroll
+          for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+            for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
+        }
+        st.m = m_next;
+      }
+      const float m_use = st.m == -INFINITY ? 0.f : st.m;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
+      if constexpr (BF16) {
+        const unsigned p01 = bf16_pack2(p[0], p[1]), p23 = bf16_pack2(p[2], p[3]);
+        st.l += (bf16_value(p01 & 0xffffu) + bf16_value(p01 >> 16)) +
+                (bf16_value(p23 & 0xffffu) + bf16_value(p23 >> 16));
+        const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+#pragma unroll
+        for (int blk = 0; blk < VBLK; ++blk) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const int dw = e >> 1;
+            const unsigned lo = __builtin_amdgcn_perm(vreg[1][blk][dw], vreg[0][blk][dw], sel);
+            const unsigned hi = __builtin_amdgcn_perm(vreg[3][blk][dw], vreg[2][blk][dw], sel);
+            const s16x4 vt = __builtin_bit_cast(s16x4, u32x2{lo, hi});
+            st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, st.acc[blk][e], 0, 0, 0);
+          }
+        }
+      } else {
+        st.l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e), p[i],
+                                                                    st.acc[blk][e], 0, 0, 0);
+      }
+      if (more) load_v(nxt);
+      cur = nxt;
+    }
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+  }
+  if (live) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;  // a column before position 0: zero row
+    store_o<KV, D, BF16>(st, o_row, inv);
+  }
+}
+
 // ------------------------------------------------------- measurement kernels
 // Not part of the attention path: a plain read stream and a plain copy of a
 // known byte count, used to measure the sustainable HBM read rate of the part
@@ -1454,6 +1746,65 @@ int run_append(int variant, bool paged, bool values_only, const void* q_raw, con
   return GQA_OK;
 }
 
+typedef void (*PrefillFn)(PrefillArgs);
+
+template <int KV, int D>
+PrefillFn pick_prefill(bool paged, bool bf16) {
+  if (paged)
+    return bf16 ? gqa_prefill_kernel<KV, D, true, true> : gqa_prefill_kernel<KV, D, true, false>;
+  return bf16 ? gqa_prefill_kernel<KV, D, false, true> : gqa_prefill_kernel<KV, D, false, false>;
+}
+
+constexpr int kMaxPrefillRows = 1 << 24;  // query rows per call
+constexpr int kProfPrefill = 9;           // profiling kinds 9 (sliding), 10 (global)
+
+int run_prefill(int variant, bool paged, const void* q, const void* k, const void* v,
+                const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                int32_t num_pages, int32_t dtype, void* stream_) {
+  if (!q || !k || !v || !cu_q || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
+  VariantInfo vi;
+  if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
+  if (B < 1 || B > kMaxBatch || N < 1 || N > kMaxPrefillRows) return GQA_ERR_SHAPE;
+  int cap;
+  if (paged) {
+    if (max_pages < 1 || max_pages > kMaxSeq / kPage || num_pages < 1) return GQA_ERR_SHAPE;
+    cap = max_pages * kPage;
+  } else {
+    if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
+    cap = S_max;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGN;
+  PrefillArgs pa;
+  pa.q = static_cast<const char*>(q);
+  pa.k = static_cast<const char*>(k);
+  pa.v = static_cast<const char*>(v);
+  pa.cu_q = cu_q;
+  pa.seq_lens = seq_lens;
+  pa.block_table = block_table;
+  pa.o = static_cast<char*>(o);
+  pa.B = B;
+  pa.N = N;
+  pa.cap = cap;
+  pa.max_pages = paged ? max_pages : 0;
+  pa.num_pages = paged ? num_pages : 0;
+  pa.window = vi.window;
+  const bool bf16 = dtype == GQA_BF16;
+  PrefillFn fn = variant == GQA_SLIDING ? pick_prefill<16, 256>(paged, bf16)
+                                        : pick_prefill<4, 512>(paged, bf16);
+  // an upper bound of the work-groups sum_b ceil(T_b*G/64): the rest exit at once
+  const int G = kHeads / vi.KV;
+  const unsigned grid_x = (unsigned)(((int64_t)N * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg + B);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  ProfRec* pr = prof_slot(kProfPrefill + variant);
+  if (pr) hipEventRecord(pr->start, stream);
+  hipLaunchKernelGGL(fn, dim3(grid_x, (unsigned)vi.KV), dim3(kThreads), 0, stream, pa);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  if (pr) hipEventRecord(pr->stop, stream);
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1592,6 +1943,36 @@ int gqa_append_global_k_eq_v_paged(const void* q_raw, const void* k_raw, const v
                                    void* stream) {
   return run_append(GQA_GLOBAL, true, true, q_raw, k_raw, nullptr, w_q, w_k, block_table,
                     max_pages, seq_lens, q_out, nullptr, v_pool, B, 0, num_pages, dtype, stream);
+}
+
+int gqa_prefill_sliding(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                        const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                        int32_t dtype, void* stream) {
+  return run_prefill(GQA_SLIDING, false, q, k, v, nullptr, 0, cu_q, seq_lens, o, B, N, S_max, 0,
+                     dtype, stream);
+}
+
+int gqa_prefill_global(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                       const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                       int32_t dtype, void* stream) {
+  return run_prefill(GQA_GLOBAL, false, q, k, v, nullptr, 0, cu_q, seq_lens, o, B, N, S_max, 0,
+                     dtype, stream);
+}
+
+int gqa_prefill_sliding_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                              const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                              int32_t num_pages, int32_t dtype, void* stream) {
+  return run_prefill(GQA_SLIDING, true, q, k_pool, v_pool, block_table, max_pages, cu_q,
+                     seq_lens, o, B, N, 0, num_pages, dtype, stream);
+}
+
+int gqa_prefill_global_paged(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                             int32_t num_pages, int32_t dtype, void* stream) {
+  return run_prefill(GQA_GLOBAL, true, q, k_pool, v_pool, block_table, max_pages, cu_q, seq_lens,
+                     o, B, N, 0, num_pages, dtype, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity) {

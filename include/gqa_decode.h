@@ -208,6 +208,42 @@ int gqa_append_global_k_eq_v_paged(const void* q_raw, const void* k_raw, const v
                                    void* v_pool, int32_t B, int32_t num_pages, int32_t dtype,
                                    void* stream);
 
+/* Prefill / chunked prefill: attention of a chunk of new tokens per sequence
+ * whose K/V rows are already in the cache (the architecture page, "Prefill,
+ * Cache, and Long Context", and the masks of its compact forward pass:
+ * positions = past_seen_tokens + arange(T_current); full layers keep keys
+ * s <= t, sliding layers t - 1024 < s <= t; K/V appended before attention).
+ * Sequence b holds seq_lens[b] positions; its T_b = cu_q[b+1] - cu_q[b] query
+ * rows are its last T_b positions, so query row n = cu_q[b] + t sits at
+ *   p = seq_lens[b] - T_b + t
+ * and, for every head h (kv head h/2 sliding, h/8 global, scale 1),
+ *   o[n,h] = sum_s softmax_s(<q[n,h], k[b,s,h/G]>) * v[b,s,h/G]
+ * over s in [max(0, p - 1023), p] (sliding) or [0, p] (global).
+ * Arguments: q, o [N,32,D] (packed query rows of all sequences); cu_q [B+1]
+ * int32 (cu_q[0] = 0, non-decreasing, cu_q[B] = N); seq_lens [B] int32; the
+ * cache as in the decode calls (contiguous [B,S_max,KV,D] or paged pools with
+ * block_table).  No workspace.  Host-checked: pointers, 1 <= B <= 256,
+ * 1 <= N <= 2^24, the capacity, dtype, 16-byte alignment (status as the
+ * decode calls).  Device-resident preconditions: cu_q as stated,
+ * T_b <= seq_lens[b] <= capacity, block-table entries of the attended pages
+ * in [0, num_pages).  Rows whose position would be negative are zero;
+ * seq_lens is clamped to the capacity; a page id outside the pool masks its
+ * keys.  Softmax in fp32, P rounded to bf16 for bf16 inputs. */
+int gqa_prefill_sliding(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                        const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                        int32_t dtype, void* stream);
+int gqa_prefill_global(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                       const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                       int32_t dtype, void* stream);
+int gqa_prefill_sliding_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                              const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                              int32_t num_pages, int32_t dtype, void* stream);
+int gqa_prefill_global_paged(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                             int32_t num_pages, int32_t dtype, void* stream);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:
@@ -252,7 +288,8 @@ int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
  * and reports, per kernel kind, the number of launches and their summed
  * duration in milliseconds (kind 2*variant: main kernel of that variant,
  * 2*variant+1: its combine kernel, 4+variant: its append kernel; the
- * values-only global calls: 6 main, 7 combine, 8 append); it also
+ * values-only global calls: 6 main, 7 combine, 8 append; prefill: 9+variant);
+ * it also
  * disables recording and releases
  * the events.  Measurement only: not thread-safe, not for captured graphs. */
 int gqa_profile_begin(int32_t capacity);

@@ -305,6 +305,25 @@ def make_prefill_case(variant: str, dtype: str, cap: int, seq_lens, q_lens, page
                        c.seq_lens, c.block_table, cap, W)
 
 
+# Prefill workloads (no page names one; shapes inside the Spec's domain): a
+# chunk of T new tokens after a cached past, every sequence alike.
+PREFILL_WORKLOADS = {
+    "sliding_bf16_prefill_b8_past4096_chunk2048": dict(variant="sliding", dtype="bf16", B=8,
+                                                        past=4096, chunk=2048, paged=False),
+    "global_bf16_prefill_b2_past8192_chunk2048_paged": dict(variant="global", dtype="bf16", B=2,
+                                                            past=8192, chunk=2048, paged=True),
+}
+
+
+def make_prefill_workload(name: str, seed: int = 0, device="cpu",
+                          fill: float = float("nan")) -> PrefillCase:
+    w = PREFILL_WORKLOADS[name]
+    L = w["past"] + w["chunk"]
+    cap = (L + PAGE - 1) // PAGE * PAGE
+    return make_prefill_case(w["variant"], w["dtype"], cap, [L] * w["B"], [w["chunk"]] * w["B"],
+                             paged=w["paged"], seed=seed, device=device, fill=fill)
+
+
 def make_workload(name: str, seed: int = 0, device="cpu", fill: float = float("nan"),
                   B: int | None = None, window: int | None = None) -> Case:
     """One of WORKLOADS by name (B may be cut down for a quick CPU-sized run; `window`
@@ -335,7 +354,8 @@ def expected_kv_bytes(name: str) -> float:
     return w["B"] * n * KV * D * 2 * eb
 
 
-__all__ = ["Case", "make_case", "make_workload", "PrefillCase", "make_prefill_case", "WORKLOADS", "VARIANTS", "to_numpy",
+__all__ = ["Case", "make_case", "make_workload", "PrefillCase", "make_prefill_case",
+           "PREFILL_WORKLOADS", "make_prefill_workload", "WORKLOADS", "VARIANTS", "to_numpy",
            "draw_seq_lens", "rms_unit", "expected_kv_bytes", "HEADS", "PAGE"]
 
 if __name__ == "__main__":  # pragma: no cover - quick look at the workloads

@@ -188,6 +188,26 @@ def test_values_only_arguments_fail_before_launch(lib):
     assert ap(ok, ok, ok, ok, None, 8, ok, ok, ok, 4, 8, 1, None) == -1
 
 
+def test_prefill_arguments_fail_before_launch(lib):
+    P = ctypes.c_void_p
+    ok, mis = P(0x10000), P(0x10008)
+    f, fp = lib.gqa_prefill_sliding, lib.gqa_prefill_global_paged
+    # f(q, k, v, cu_q, seq_lens, o, B, N, S_max, dtype, stream)
+    assert f(ok, ok, ok, None, ok, ok, 2, 64, 128, 1, None) == -1   # cu_q is required
+    assert f(ok, ok, ok, ok, ok, ok, 0, 64, 128, 1, None) == -2
+    assert f(ok, ok, ok, ok, ok, ok, 257, 64, 128, 1, None) == -2
+    assert f(ok, ok, ok, ok, ok, ok, 2, 0, 128, 1, None) == -2      # no query rows
+    assert f(ok, ok, ok, ok, ok, ok, 2, (1 << 24) + 1, 128, 1, None) == -2
+    assert f(ok, ok, ok, ok, ok, ok, 2, 64, 262145, 1, None) == -2
+    assert f(ok, ok, ok, ok, ok, ok, 2, 64, 128, 3, None) == -3
+    assert f(mis, ok, ok, ok, ok, ok, 2, 64, 128, 1, None) == -4
+    assert f(ok, ok, ok, ok, ok, mis, 2, 64, 128, 1, None) == -4
+    # fp(q, k_pool, v_pool, block_table, max_pages, cu_q, seq_lens, o, B, N, num_pages, dtype, s)
+    assert fp(ok, ok, ok, None, 8, ok, ok, ok, 2, 64, 8, 1, None) == -1
+    assert fp(ok, ok, ok, ok, 0, ok, ok, ok, 2, 64, 8, 1, None) == -2
+    assert fp(ok, ok, ok, ok, 8, ok, ok, ok, 2, 64, 0, 1, None) == -2
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     q = torch.zeros(1, 32, 256, dtype=torch.bfloat16)

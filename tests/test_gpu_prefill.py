@@ -1,0 +1,126 @@
+"""Prefill / chunked prefill (a chunk of new tokens per sequence, causal and
+sliding masks) vs the fp64 oracle, through the C ABI, on an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_slidingdecodegqa_amd as gqa
+import oracle
+import synth
+from gpu_cases import TOL, max_err, to_f64
+
+pytestmark = pytest.mark.gpu
+HEADS = 32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but no GPU is visible")
+    gqa.library()
+
+
+def to_gpu(c: synth.PrefillCase) -> synth.PrefillCase:
+    d = "cuda"
+    return synth.PrefillCase(c.variant, c.dtype, c.q.to(d), c.k.to(d), c.v.to(d), c.cu_q.to(d),
+                             c.seq_lens.to(d),
+                             None if c.block_table is None else c.block_table.to(d), c.cap,
+                             c.window)
+
+
+def to_cpu(c: synth.PrefillCase) -> synth.PrefillCase:
+    return synth.PrefillCase(c.variant, c.dtype, c.q.cpu(), c.k.cpu(), c.v.cpu(), c.cu_q.cpu(),
+                             c.seq_lens.cpu(),
+                             None if c.block_table is None else c.block_table.cpu(), c.cap,
+                             c.window)
+
+
+def hip_prefill(c: synth.PrefillCase, o=None, stream=None) -> torch.Tensor:
+    fn = gqa.gqa_prefill_sliding if c.variant == "sliding" else gqa.gqa_prefill_global
+    return fn(c.q, c.k, c.v, c.cu_q, c.seq_lens, block_table=c.block_table, o=o, stream=stream)
+
+
+def oracle_prefill(c: synth.PrefillCase, rows=None) -> np.ndarray:
+    n = synth.to_numpy
+    bt = None if c.block_table is None else n(c.block_table)
+    return oracle.gqa_prefill((c.KV, c.D, c.window), n(c.q), n(c.k), n(c.v), n(c.cu_q),
+                              n(c.seq_lens), block_table=bt, rows=rows, nthreads=16)
+
+
+# lengths: a chunk after a long past (crossing the window), a fresh prompt, a
+# single token, an empty chunk, a chunk starting at position 0 with the cache
+# full
+CASES = {
+    "sliding": dict(cap=2112, seq_lens=[1300, 40, 7, 900, 2100], q_lens=[77, 40, 1, 0, 300]),
+    "global": dict(cap=720, seq_lens=[700, 33, 1, 260, 64], q_lens=[50, 33, 1, 0, 64]),
+}
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_prefill_parity(variant, dtype, paged):
+    kw = CASES[variant]
+    c = synth.make_prefill_case(variant, dtype, kw["cap"], kw["seq_lens"], kw["q_lens"],
+                                paged=paged, seed=500, extra_pages=3)
+    got = to_f64(hip_prefill(to_gpu(c)))
+    assert np.isfinite(got).all()  # NaN outside every attended range is never read
+    err = max_err(got, oracle_prefill(c))
+    assert err <= TOL[dtype], err
+
+
+def test_prefill_fresh_prompt_first_token_exact():
+    # position 0 attends only to itself: o = v[0] bit for bit
+    for variant, G in (("sliding", 2), ("global", 8)):
+        c = synth.make_prefill_case(variant, "bf16", 64, [20, 64], [20, 64], seed=501)
+        got = hip_prefill(to_gpu(c)).cpu()
+        for b, n in enumerate((0, 20)):
+            for h in range(HEADS):
+                assert torch.equal(got[n, h], c.v[b, 0, h // G])
+
+
+def test_prefill_paged_equals_contiguous():
+    for variant in ("sliding", "global"):
+        kw = dict(seed=502, fill=0.0)
+        a = synth.make_prefill_case(variant, "bf16", 1040, [1040, 300], [200, 300], **kw)
+        b = synth.make_prefill_case(variant, "bf16", 1040, [1040, 300], [200, 300], paged=True,
+                                    **kw)
+        assert torch.equal(hip_prefill(to_gpu(a)).cpu(), hip_prefill(to_gpu(b)).cpu())
+
+
+def test_prefill_deterministic_on_a_side_stream():
+    c = to_gpu(synth.make_prefill_case("global", "bf16", 1024, [1024, 512], [300, 100],
+                                       seed=503))
+    a = hip_prefill(c).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o = torch.full_like(c.q, float("nan"))
+        b = hip_prefill(c, o=o, stream=s)
+    s.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_prefill_profile_kind():
+    c = to_gpu(synth.make_prefill_case("sliding", "bf16", 256, [256], [64], seed=504))
+    gqa.profile_begin(8)
+    hip_prefill(c)
+    res = gqa.profile_read()
+    assert res[("sliding", "prefill")][0] == 1 and res[("global", "prefill")][0] == 0
+
+
+@pytest.mark.parametrize("name", sorted(synth.PREFILL_WORKLOADS))
+def test_prefill_workload_sampled(name):
+    c = synth.make_prefill_workload(name, seed=0, device="cuda")
+    got = hip_prefill(c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got.float()).all()
+    host = to_cpu(c)
+    cu = host.cu_q.tolist()
+    # first, middle and last query rows of the first and last sequence, a few heads
+    ns = sorted({cu[0], (cu[0] + cu[1]) // 2, cu[1] - 1, cu[-2], cu[-1] - 1})
+    rows = [(n, h) for n in ns for h in (0, 7, 8, 31)]
+    ref = oracle_prefill(host, rows=rows)
+    g = to_f64(got)
+    for i, (n, h) in enumerate(rows):
+        assert max_err(g[n, h], ref[i]) <= TOL["bf16"], (name, n, h)
