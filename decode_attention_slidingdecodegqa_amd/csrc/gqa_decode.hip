@@ -1162,11 +1162,13 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
 // attends to the keys its mask keeps (global: s <= p; sliding: p - W < s <= p).
 //
 // Work: the query rows of one (sequence, kv head g) form T_b*G columns
-// (token-major, the G heads of a token adjacent); a wave takes 16 of them and
-// runs the decode tile loop over the union of their key ranges with all 16
-// MFMA columns in use, each column masked to its own range.  A work-group's
-// four waves take consecutive column blocks of the same (b, g), so they read
-// the same K/V tiles close together in time.
+// (token-major, the G heads of a token adjacent); a wave takes 16 of them, a
+// work-group 64.  The work-group walks the union of its columns' key ranges
+// in tiles of 16 positions: each K/V tile is fetched once with coalesced
+// 16-byte loads into a double-buffered LDS tile (chunks XOR-swizzled by row so
+// both MFMA operand layouts read conflict-free), which all four waves use with
+// every MFMA column masked to its own range.  Work-groups of one (b, g) are
+// placed on one XCD so their shared tiles stay in that XCD's L2.
 
 struct PrefillArgs {
   const char* q;
@@ -1181,10 +1183,11 @@ struct PrefillArgs {
 
 constexpr int kPrefillCols = 16;                  // query columns per wave
 constexpr int kPrefillColsPerWg = kPrefillCols * kWaves;
+constexpr int kXcds = 8;
 
 template <int KV, bool BF16>
 constexpr int prefill_waves_per_simd() {
-  return KV == 16 ? 2 : 1;
+  return (KV == 16 && BF16) ? 2 : 1;
 }
 
 template <int KV, int D, bool PAGED, bool BF16>
@@ -1194,7 +1197,9 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
                 VBLK = Gm::VBLK;
   constexpr size_t POS = Gm::POS;
-  constexpr int QPL = kPrefillCols * NCH / 64;  // query chunks per lane when staging
+  constexpr int TILE_BYTES = kTile * ROW;          // one K (or V) tile in LDS
+  constexpr int LDPT = 2 * kTile * NCH / kThreads;  // 16-byte chunks per thread per K+V tile
+  static_assert(LDPT * kThreads == 2 * kTile * NCH, "tile split");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;
@@ -1205,7 +1210,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   __shared__ int s_wg0[kMaxBatch + 1];
   __shared__ int s_cu[kMaxBatch + 1];
   __shared__ int s_len[kMaxBatch];
-  __shared__ u32x4 s_q[kWaves][kPrefillCols * NCH];
+  __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE_BYTES];  // [buffer][K, V]
   if (threadIdx.x < 64) {
     int cnt[4];
 #pragma unroll
@@ -1237,9 +1242,12 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
     }
     if (lane == 63) s_wg0[a.B] = incl;
   }
-  __syncthreads();  // the only barrier: waves may leave below
-  const int wg = blockIdx.x;
-  if (wg >= s_wg0[a.B]) return;
+  __syncthreads();
+  // XCD-aware order: the hardware deals work-groups round-robin over the XCDs,
+  // so consecutive logical work-groups (same (b, g), neighbouring columns)
+  // are given block ids that land on one XCD (gridDim.x is a multiple of 8)
+  const int wg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (wg >= s_wg0[a.B]) return;  // the whole work-group leaves together
   int b = 0;
   {
     int lo_b = 0, hi_b = a.B - 1;
@@ -1253,25 +1261,25 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   const int cu = s_cu[b];
   const int T = s_cu[b + 1] - cu;
   const int cols = T * G;
-  const int col0 = ((wg - s_wg0[b]) * kWaves + wave) * kPrefillCols;
-  if (col0 >= cols) return;
   const int L = min(s_len[b], a.cap);  // clamped for memory safety
+  const int wcol0 = (wg - s_wg0[b]) * kPrefillColsPerWg;  // < cols
+  const int col0 = wcol0 + wave * kPrefillCols;
+  const bool wave_live = col0 < cols;  // dead waves still take part in the barriers
 
   // ---- this lane's column (n = r): token, head, position, key range
   const int col = col0 + r;
   const bool live = col < cols;
-  const int t_n = (live ? col : cols - 1) / G;
-  const int head = g * G + (live ? col : cols - 1) % G;
+  const int cl = live ? col : cols - 1;
+  const int t_n = cl / G;
+  const int head = g * G + cl % G;
   const int p_n = L - T + t_n;
   const int lo_n = a.window > 0 ? max(0, p_n - a.window + 1) : 0;
-  // the wave's key range: the union over its columns (token-major: first and last)
-  const int t_first = col0 / G;
-  const int t_last = (min(col0 + kPrefillCols, cols) - 1) / G;
-  const int p_last = L - T + t_last;
-  const int p_first = max(L - T + t_first, 0);
+  // the work-group's key range: the union over its columns (token-major)
+  const int wcol_end = min(wcol0 + kPrefillColsPerWg, cols);
+  const int p_last = L - T + (wcol_end - 1) / G;
+  const int p_first = max(L - T + wcol0 / G, 0);
   const int range_lo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
   const int range_hi = p_last;  // inclusive
-  char* o_row = a.o + ((size_t)(cu + t_n) * kHeads + head) * ROW;
 
   WaveState<KV, D, BF16> st;
 #pragma unroll
@@ -1282,168 +1290,176 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   st.l = 0.f;
 
   if (range_hi >= 0) {
-    // ---- stage the 16 columns' query rows in the wave's LDS slice
-    u32x4* myq = s_q[wave];
-    {
-      u32x4 qs[QPL];
+    // ---- the lane's query operands: column r, chunks 4c+j (bf16: registers;
+    // f32, a parity case, reads them from global memory at every tile)
+    u32x4 qreg[BF16 ? KCH : 1];
+    const char* qsrc = a.q + ((size_t)(cu + t_n) * kHeads + head) * ROW;
+    if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < QPL; ++i) {
-        const int c = lane + 64 * i;     // chunk c of the slice: column c / NCH
-        const int cn = col0 + c / NCH;
-        const int cc = min(cn, cols - 1);
-        const char* src = a.q + ((size_t)(cu + cc / G) * kHeads + g * G + cc % G) * ROW;
-        qs[i] = cn < cols ? load16(src + (size_t)(c % NCH) * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < QPL; ++i) myq[lane + 64 * i] = qs[i];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+      for (int c = 0; c < KCH; ++c)
+        qreg[c] = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
-    const u32x4* qrow = myq + r * NCH;
     const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
 
-    struct TileAt {
-      const char* kb;
-      const char* vb;
-      int pos0;
-      bool ok;
-    };
-    auto tile_at = [&](int tile) {
-      TileAt ta;
-      ta.pos0 = tile * kTile;
-      size_t off;
+    // ---- cooperative tile fetch: thread t takes chunks t + 256u of the K+V
+    // tile (chunk -> K/V, row, column chunk), stores them XOR-swizzled by row
+    u32x4 ld[LDPT];
+    auto fetch = [&](int tile) {
+      const int pos0 = tile * kTile;
+      size_t base;
+      bool ok = true;
       if constexpr (PAGED) {
         const int page = bt[tile];
-        ta.ok = page >= 0 && page < a.num_pages;
-        off = ((size_t)(ta.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+        ok = page >= 0 && page < a.num_pages;
+        base = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
       } else {
-        ta.ok = true;
-        off = (((size_t)b * a.cap + ta.pos0) * KV + g) * (size_t)ROW;
+        base = (((size_t)b * a.cap + pos0) * KV + g) * (size_t)ROW;
       }
-      ta.kb = a.k + off;
-      ta.vb = a.v + off;
-      return ta;
-    };
-    auto clamp_row = [&](int pos0, int row) {
-      const int p = min(max(pos0 + row, range_lo), range_hi);
-      return p - pos0;
-    };
-    u32x4 kreg[KCH];
-    u32x4 vreg[4][VBLK];
-    auto load_k = [&](const TileAt& ta) {
-      const char* rowp = ta.kb + (size_t)clamp_row(ta.pos0, r) * POS;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) kreg[c] = load16(rowp + (4 * c + j) * 16);
+      for (int u = 0; u < LDPT; ++u) {
+        const int q = threadIdx.x + kThreads * u;
+        const int which = q / (kTile * NCH);  // 0: K, 1: V
+        const int row = (q / NCH) % kTile;
+        const int c = q % NCH;
+        const int p = min(max(pos0 + row, range_lo), range_hi);  // clamped, never unattended
+        const char* src = (which ? a.v : a.k) + base + (size_t)(p - pos0) * POS + c * 16;
+        ld[u] = load16(src);
+      }
+      return ok;
     };
-    auto load_v = [&](const TileAt& ta) {
+    auto stash = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* rowp = ta.vb + (size_t)clamp_row(ta.pos0, 4 * j + i) * POS;
-#pragma unroll
-        for (int blk = 0; blk < VBLK; ++blk) vreg[i][blk] = load16(rowp + (r + 16 * blk) * 16);
+      for (int u = 0; u < LDPT; ++u) {
+        const int q = threadIdx.x + kThreads * u;
+        const int which = q / (kTile * NCH);
+        const int row = (q / NCH) % kTile;
+        const int c = q % NCH;
+        *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * ROW + ((c ^ row) << 4)]) = ld[u];
       }
     };
 
     const int tile_begin = range_lo / kTile, tile_end = range_hi / kTile;  // inclusive
-    TileAt cur = tile_at(tile_begin);
-    load_k(cur);
-    load_v(cur);
+    bool ok_cur = fetch(tile_begin);
+    stash(0);
+    __syncthreads();
     for (int tile = tile_begin; tile <= tile_end; ++tile) {
+      const int buf = (tile - tile_begin) & 1;
       const bool more = tile < tile_end;
-      const TileAt nxt = more ? tile_at(tile + 1) : cur;
-      // logits z[key 4j+i][column r]
-      f32x4 z;
-      {
-        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF16) {
+      bool ok_nxt = true;
+      if (more) ok_nxt = fetch(tile + 1);
+      if (wave_live) {
+        const char* kt = s_kv[buf][0];
+        const char* vt = s_kv[buf][1];
+        // logits z[key 4j+i][column r]
+        f32x4 z;
+        {
+          f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+          auto kop = [&](int c) {
+            return *reinterpret_cast<const u32x4*>(kt + r * ROW + (((4 * c + j) ^ r) << 4));
+          };
+          if constexpr (BF16) {
 #pragma unroll
-          for (int c = 0; c < KCH; c += 2) {
-            z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[c]),
-                                                         __builtin_bit_cast(bf16x8, qrow[4 * c + j]),
-                                                         z0, 0, 0, 0);
-            z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, kreg[c + 1]),
-                __builtin_bit_cast(bf16x8, qrow[4 * c + 4 + j]), z1, 0, 0, 0);
-          }
-        } else {
+            for (int c = 0; c < KCH; c += 2) {
+              z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop(c)),
+                                                           __builtin_bit_cast(bf16x8, qreg[c]), z0,
+                                                           0, 0, 0);
+              z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop(c + 1)),
+                                                           __builtin_bit_cast(bf16x8, qreg[c + 1]),
+                                                           z1, 0, 0, 0);
+            }
+          } else {
 #pragma unroll
-          for (int c = 0; c < KCH; ++c) {
-            const u32x4 qc = qrow[4 * c + j];
+            for (int c = 0; c < KCH; ++c) {
+              const u32x4 kc = kop(c);
+              const u32x4 qc = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-              z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e), chunk_f32(qc, e),
-                                                        z0, 0, 0, 0);
-              z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e + 1),
-                                                        chunk_f32(qc, e + 1), z1, 0, 0, 0);
+              for (int e = 0; e < 4; e += 2) {
+                z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e), chunk_f32(qc, e), z0,
+                                                          0, 0, 0);
+                z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e + 1),
+                                                          chunk_f32(qc, e + 1), z1, 0, 0, 0);
+              }
             }
           }
+          z = z0 + z1;
         }
-        z = z0 + z1;
-      }
-      if (more) load_k(nxt);
-      // each column keeps the keys of its own mask
+        // each column keeps the keys of its own mask
+        const int pos0 = tile * kTile;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = cur.pos0 + 4 * j + i;
-        if (!(cur.ok && live && s >= lo_n && s <= p_n)) z[i] = -INFINITY;
-      }
-      float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const bool grow = tmax > st.m + kRescaleGap;
-      if (__any(grow)) {
-        const float m_next = grow ? tmax : st.m;
-        const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
-        if (grow) {
-          st.l *= alpha;
-#pragma unroll
-          for (int blk = 0; blk < VBLK; ++blk)
-#pragma unroll
-            for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const int s = pos0 + 4 * j + i;
+          if (!(ok_cur && live && s >= lo_n && s <= p_n)) z[i] = -INFINITY;
         }
-        st.m = m_next;
-      }
-      const float m_use = st.m == -INFINITY ? 0.f : st.m;
-      float p[4];
+        float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool grow = tmax > st.m + kRescaleGap;
+        if (__any(grow)) {
+          const float m_next = grow ? tmax : st.m;
+          const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+          if (grow) {
+            st.l *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
-      if constexpr (BF16) {
-        const unsigned p01 = bf16_pack2(p[0], p[1]), p23 = bf16_pack2(p[2], p[3]);
-        st.l += (bf16_value(p01 & 0xffffu) + bf16_value(p01 >> 16)) +
-                (bf16_value(p23 & 0xffffu) + bf16_value(p23 >> 16));
-        const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+            for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
-        for (int blk = 0; blk < VBLK; ++blk) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const int dw = e >> 1;
-            const unsigned lo = __builtin_amdgcn_perm(vreg[1][blk][dw], vreg[0][blk][dw], sel);
-            const unsigned hi = __builtin_amdgcn_perm(vreg[3][blk][dw], vreg[2][blk][dw], sel);
-            const s16x4 vt = __builtin_bit_cast(s16x4, u32x2{lo, hi});
-            st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, st.acc[blk][e], 0, 0, 0);
+              for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
           }
+          st.m = m_next;
         }
-      } else {
-        st.l += (p[0] + p[1]) + (p[2] + p[3]);
+        const float m_use = st.m == -INFINITY ? 0.f : st.m;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
+        // value operands: rows 4j+i, chunks r+16*blk
+        u32x4 vreg[4][VBLK];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int blk = 0; blk < VBLK; ++blk)
+          for (int blk = 0; blk < VBLK; ++blk) {
+            const int row = 4 * j + i;
+            vreg[i][blk] =
+                *reinterpret_cast<const u32x4*>(vt + row * ROW + (((r + 16 * blk) ^ row) << 4));
+          }
+        if constexpr (BF16) {
+          const unsigned p01 = bf16_pack2(p[0], p[1]), p23 = bf16_pack2(p[2], p[3]);
+          st.l += (bf16_value(p01 & 0xffffu) + bf16_value(p01 >> 16)) +
+                  (bf16_value(p23 & 0xffffu) + bf16_value(p23 >> 16));
+          const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e), p[i],
-                                                                    st.acc[blk][e], 0, 0, 0);
+          for (int blk = 0; blk < VBLK; ++blk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+              const int dw = e >> 1;
+              const unsigned lo = __builtin_amdgcn_perm(vreg[1][blk][dw], vreg[0][blk][dw], sel);
+              const unsigned hi = __builtin_amdgcn_perm(vreg[3][blk][dw], vreg[2][blk][dw], sel);
+              const s16x4 vtr = __builtin_bit_cast(s16x4, u32x2{lo, hi});
+              st.acc[blk][e] =
+                  __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vtr, pt, st.acc[blk][e], 0, 0, 0);
+            }
+          }
+        } else {
+          st.l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e),
+                                                                      p[i], st.acc[blk][e], 0, 0, 0);
+        }
       }
-      if (more) load_v(nxt);
-      cur = nxt;
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+      ok_cur = ok_nxt;
     }
     st.l += __shfl_xor(st.l, 16);
     st.l += __shfl_xor(st.l, 32);
   }
   if (live) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;  // a column before position 0: zero row
-    store_o<KV, D, BF16>(st, o_row, inv);
+    store_o<KV, D, BF16>(st, a.o + ((size_t)(cu + t_n) * kHeads + head) * ROW, inv);
   }
 }
 
@@ -1795,7 +1811,9 @@ int run_prefill(int variant, bool paged, const void* q, const void* k, const voi
                                         : pick_prefill<4, 512>(paged, bf16);
   // an upper bound of the work-groups sum_b ceil(T_b*G/64): the rest exit at once
   const int G = kHeads / vi.KV;
-  const unsigned grid_x = (unsigned)(((int64_t)N * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg + B);
+  int64_t n_wg = ((int64_t)N * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg + B;
+  n_wg = (n_wg + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD remap needs a multiple of 8
+  const unsigned grid_x = (unsigned)n_wg;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   ProfRec* pr = prof_slot(kProfPrefill + variant);
   if (pr) hipEventRecord(pr->start, stream);
