@@ -1164,11 +1164,14 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
 // Work: the query rows of one (sequence, kv head g) form T_b*G columns
 // (token-major, the G heads of a token adjacent); a wave takes 16 of them, a
 // work-group 64.  The work-group walks the union of its columns' key ranges
-// in tiles of 16 positions: each K/V tile is fetched once with coalesced
-// 16-byte loads into a double-buffered LDS tile (chunks XOR-swizzled by row so
-// both MFMA operand layouts read conflict-free), which all four waves use with
-// every MFMA column masked to its own range.  Work-groups of one (b, g) are
-// placed on one XCD so their shared tiles stay in that XCD's L2.
+// in steps of PT positions (32 for bf16, two 16-key MFMA halves; 16 for f32):
+// each K/V step is fetched once with coalesced 16-byte loads into a
+// double-buffered LDS tile with rows padded by 16 bytes (the 16 rows one lane
+// group reads fall in distinct banks, and every operand address is a lane
+// base plus an immediate), which all four waves use with every MFMA column
+// masked to its own range.  bf16 P@V runs on 16x16x32 MFMAs over both halves
+// of a step.  Work-groups of one (b, g) are placed on one XCD so their shared
+// tiles stay in that XCD's L2.
 
 struct PrefillArgs {
   const char* q;
@@ -1197,9 +1200,13 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
                 VBLK = Gm::VBLK;
   constexpr size_t POS = Gm::POS;
-  constexpr int TILE_BYTES = kTile * ROW;          // one K (or V) tile in LDS
-  constexpr int LDPT = 2 * kTile * NCH / kThreads;  // 16-byte chunks per thread per K+V tile
-  static_assert(LDPT * kThreads == 2 * kTile * NCH, "tile split");
+  constexpr int PT = BF16 ? 32 : 16;                // key positions per step
+  constexpr int NH = PT / 16;                       // 16-key halves per step
+  constexpr int RS = ROW + 16;                      // padded LDS row stride
+  constexpr int TILE_BYTES = PT * RS;               // one K (or V) step in LDS
+  constexpr int LDPT = 2 * PT * NCH / kThreads;     // 16-byte chunks per thread per step
+  static_assert(LDPT * kThreads == 2 * PT * NCH, "step split");
+  static_assert(NCH >= 64 || (kThreads % NCH) == 0, "rows per fetch instruction");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;
@@ -1291,7 +1298,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
 
   if (range_hi >= 0) {
     // ---- the lane's query operands: column r, chunks 4c+j (bf16: registers;
-    // f32, a parity case, reads them from global memory at every tile)
+    // f32, a parity case, reads them from global memory at every step)
     u32x4 qreg[BF16 ? KCH : 1];
     const char* qsrc = a.q + ((size_t)(cu + t_n) * kHeads + head) * ROW;
     if constexpr (BF16) {
@@ -1300,77 +1307,118 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
         qreg[c] = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
     const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+    const int last_page = range_hi / kPage;
 
-    // ---- cooperative tile fetch: thread t takes chunks t + 256u of the K+V
-    // tile (chunk -> K/V, row, column chunk), stores them XOR-swizzled by row
-    u32x4 ld[LDPT];
-    auto fetch = [&](int tile) {
-      const int pos0 = tile * kTile;
-      size_t base;
-      bool ok = true;
-      if constexpr (PAGED) {
-        const int page = bt[tile];
-        ok = page >= 0 && page < a.num_pages;
-        base = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
-      } else {
-        base = (((size_t)b * a.cap + pos0) * KV + g) * (size_t)ROW;
-      }
+    // ---- cooperative step fetch.  Rows are clamped into the range (every step
+    // lies within [range_lo & ~(PT-1), range_hi], so a clamped row stays in
+    // the step's pages).  Rows of at least 1 KiB go straight to LDS (one
+    // 16-byte-per-lane LDS-DMA load per KiB: LDS address = base + 16*lane, all
+    // other addressing wave-uniform); shorter rows go through registers
+    // (thread t takes chunks t + 256u of the K+V step).
+    constexpr bool DMA = ROW % 1024 == 0;
+    constexpr int IPR = DMA ? ROW / 1024 : 1;       // DMA loads per row
+    constexpr int DMA_PER_WAVE = 2 * PT * IPR / kWaves;
+    u32x4 ld[DMA ? 1 : LDPT];
+    auto fetch = [&](int step, int& okbits, int buf) {
+      const int pos0 = step * PT;
+      size_t base[NH];
+      okbits = 0;
 #pragma unroll
-      for (int u = 0; u < LDPT; ++u) {
-        const int q = threadIdx.x + kThreads * u;
-        const int which = q / (kTile * NCH);  // 0: K, 1: V
-        const int row = (q / NCH) % kTile;
-        const int c = q % NCH;
-        const int p = min(max(pos0 + row, range_lo), range_hi);  // clamped, never unattended
-        const char* src = (which ? a.v : a.k) + base + (size_t)(p - pos0) * POS + c * 16;
-        ld[u] = load16(src);
+      for (int h = 0; h < NH; ++h) {
+        if constexpr (PAGED) {
+          const int pi = pos0 / kPage + h;
+          const int page = pi <= last_page ? bt[pi] : 0;
+          const bool ok = page >= 0 && page < a.num_pages;
+          okbits |= ok ? (1 << h) : 0;
+          base[h] = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+        } else {
+          okbits |= 1 << h;
+          base[h] = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
+        }
       }
-      return ok;
+      if constexpr (DMA) {
+#pragma unroll
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+          const int inst = wave + kWaves * i;  // wave-uniform
+          const int which = inst / (PT * IPR);
+          const int row = (inst / IPR) % PT;
+          const int part = inst % IPR;
+          const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;
+          const int h = rel >> 4;
+          const size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
+                             (size_t)(rel & 15) * POS + part * 1024;
+          __builtin_amdgcn_global_load_lds(
+              (const void*)((which ? a.v : a.k) + off + lane * 16),
+              (__attribute__((address_space(3))) void*)&s_kv[buf][which][row * RS + part * 1024],
+              16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < LDPT; ++u) {
+          const int q = threadIdx.x + kThreads * u;
+          const int which = q / (PT * NCH);  // 0: K, 1: V
+          const int row = (q / NCH) % PT;
+          const int c = q % NCH;
+          const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
+          const int h = rel >> 4;
+          size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
+                       (size_t)(rel & 15) * POS + c * 16;
+          ld[u] = load16((which ? a.v : a.k) + off);
+        }
+      }
     };
     auto stash = [&](int buf) {
+      if constexpr (!DMA) {
 #pragma unroll
-      for (int u = 0; u < LDPT; ++u) {
-        const int q = threadIdx.x + kThreads * u;
-        const int which = q / (kTile * NCH);
-        const int row = (q / NCH) % kTile;
-        const int c = q % NCH;
-        *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * ROW + ((c ^ row) << 4)]) = ld[u];
+        for (int u = 0; u < LDPT; ++u) {
+          const int q = threadIdx.x + kThreads * u;
+          const int which = q / (PT * NCH);
+          const int row = (q / NCH) % PT;
+          const int c = q % NCH;
+          *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * RS + c * 16]) = ld[u];
+        }
+      } else {
+        // the step's LDS-DMA loads have landed before the barrier that follows
+        __builtin_amdgcn_s_waitcnt(0);
       }
     };
 
-    const int tile_begin = range_lo / kTile, tile_end = range_hi / kTile;  // inclusive
-    bool ok_cur = fetch(tile_begin);
+    const int step_begin = range_lo / PT, step_end = range_hi / PT;  // inclusive
+    int ok_cur, ok_nxt = 0;
+    fetch(step_begin, ok_cur, 0);
     stash(0);
     __syncthreads();
-    for (int tile = tile_begin; tile <= tile_end; ++tile) {
-      const int buf = (tile - tile_begin) & 1;
-      const bool more = tile < tile_end;
-      bool ok_nxt = true;
-      if (more) ok_nxt = fetch(tile + 1);
+    const int kbase = r * RS + j * 16;             // key operand: row r (+16h), chunk 4c+j
+    const int vbase = 4 * j * RS + r * 16;         // value operand: rows 4j+i (+16h), chunk r+16blk
+    for (int step = step_begin; step <= step_end; ++step) {
+      const int buf = (step - step_begin) & 1;
+      const bool more = step < step_end;
+      if (more) fetch(step + 1, ok_nxt, buf ^ 1);
       if (wave_live) {
-        const char* kt = s_kv[buf][0];
-        const char* vt = s_kv[buf][1];
-        // logits z[key 4j+i][column r]
-        f32x4 z;
-        {
+        const char* kt = s_kv[buf][0] + kbase;
+        const char* vt = s_kv[buf][1] + vbase;
+        // logits z[h][key 16h+4j+i][column r]
+        f32x4 z[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
           f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-          auto kop = [&](int c) {
-            return *reinterpret_cast<const u32x4*>(kt + r * ROW + (((4 * c + j) ^ r) << 4));
-          };
+          const char* kh = kt + h * 16 * RS;
           if constexpr (BF16) {
 #pragma unroll
             for (int c = 0; c < KCH; c += 2) {
-              z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop(c)),
+              const u32x4 k0 = *reinterpret_cast<const u32x4*>(kh + c * 64);
+              const u32x4 k1 = *reinterpret_cast<const u32x4*>(kh + c * 64 + 64);
+              z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0),
                                                            __builtin_bit_cast(bf16x8, qreg[c]), z0,
                                                            0, 0, 0);
-              z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop(c + 1)),
+              z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1),
                                                            __builtin_bit_cast(bf16x8, qreg[c + 1]),
                                                            z1, 0, 0, 0);
             }
           } else {
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
-              const u32x4 kc = kop(c);
+              const u32x4 kc = *reinterpret_cast<const u32x4*>(kh + c * 64);
               const u32x4 qc = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
               for (int e = 0; e < 4; e += 2) {
@@ -1381,16 +1429,19 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
               }
             }
           }
-          z = z0 + z1;
+          z[h] = z0 + z1;
         }
         // each column keeps the keys of its own mask
-        const int pos0 = tile * kTile;
+        const int pos0 = step * PT;
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = pos0 + 4 * j + i;
-          if (!(ok_cur && live && s >= lo_n && s <= p_n)) z[i] = -INFINITY;
-        }
-        float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = pos0 + 16 * h + 4 * j + i;
+            if (!(((ok_cur >> h) & 1) && live && s >= lo_n && s <= p_n)) z[h][i] = -INFINITY;
+            tmax = fmaxf(tmax, z[h][i]);
+          }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const bool grow = tmax > st.m + kRescaleGap;
@@ -1407,47 +1458,60 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
           st.m = m_next;
         }
         const float m_use = st.m == -INFINITY ? 0.f : st.m;
-        float p[4];
+        float p[NH][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = exp2_fast((z[i] - m_use) * kLog2e);
-        // value operands: rows 4j+i, chunks r+16*blk
-        u32x4 vreg[4][VBLK];
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int blk = 0; blk < VBLK; ++blk) {
-            const int row = 4 * j + i;
-            vreg[i][blk] =
-                *reinterpret_cast<const u32x4*>(vt + row * ROW + (((r + 16 * blk) ^ row) << 4));
-          }
+          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast((z[h][i] - m_use) * kLog2e);
         if constexpr (BF16) {
-          const unsigned p01 = bf16_pack2(p[0], p[1]), p23 = bf16_pack2(p[2], p[3]);
-          st.l += (bf16_value(p01 & 0xffffu) + bf16_value(p01 >> 16)) +
-                  (bf16_value(p23 & 0xffffu) + bf16_value(p23 >> 16));
-          const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+          // P^T operand: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
+          u32x4 pt;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            pt[2 * h] = bf16_pack2(p[h][0], p[h][1]);
+            pt[2 * h + 1] = bf16_pack2(p[h][2], p[h][3]);
+            st.l += (bf16_value(pt[2 * h] & 0xffffu) + bf16_value(pt[2 * h] >> 16)) +
+                    (bf16_value(pt[2 * h + 1] & 0xffffu) + bf16_value(pt[2 * h + 1] >> 16));
+          }
 #pragma unroll
           for (int blk = 0; blk < VBLK; ++blk) {
+            u32x4 vr[2][4];  // value rows 16h+4j+i, chunk r+16*blk
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                vr[h][i] = *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RS + blk * 256);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
               const int dw = e >> 1;
-              const unsigned lo = __builtin_amdgcn_perm(vreg[1][blk][dw], vreg[0][blk][dw], sel);
-              const unsigned hi = __builtin_amdgcn_perm(vreg[3][blk][dw], vreg[2][blk][dw], sel);
-              const s16x4 vtr = __builtin_bit_cast(s16x4, u32x2{lo, hi});
-              st.acc[blk][e] =
-                  __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vtr, pt, st.acc[blk][e], 0, 0, 0);
+              u32x4 vtr;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                vtr[2 * h] = __builtin_amdgcn_perm(vr[h][1][dw], vr[h][0][dw], sel);
+                vtr[2 * h + 1] = __builtin_amdgcn_perm(vr[h][3][dw], vr[h][2][dw], sel);
+              }
+              st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, vtr), __builtin_bit_cast(bf16x8, pt), st.acc[blk][e],
+                  0, 0, 0);
             }
           }
         } else {
-          st.l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int h = 0; h < NH; ++h) {
+            st.l += (p[h][0] + p[h][1]) + (p[h][2] + p[h][3]);
 #pragma unroll
-            for (int blk = 0; blk < VBLK; ++blk)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vreg[i][blk], e),
-                                                                      p[i], st.acc[blk][e], 0, 0, 0);
+              for (int blk = 0; blk < VBLK; ++blk) {
+                const u32x4 vc =
+                    *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RS + blk * 256);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vc, e), p[h][i],
+                                                                        st.acc[blk][e], 0, 0, 0);
+              }
+          }
         }
       }
       if (more) stash(buf ^ 1);
