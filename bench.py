@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = ("decode-attn K/V read GB/s and % of HBM peak; µs per call "
           "(sliding B=256, global B=32)")
 SLIDING = "sliding_bf16_b256_s8192"
@@ -36,8 +37,9 @@ GLOBAL = "global_bf16_b32_paged_s16k_128k"
 # windows of the Retrofit Plan page's progressive window table)
 SWEEP_WINDOWS = (2048, 4096, 8192)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sliding_b256_global_b32_paged.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd", "csrc",
-                             "gqa_decode.hip")
+# the sources of the decode and append kernels (the profiled ones)
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd", "csrc", f)
+                  for f in ("gqa_common.h", "gqa_decode.hip")]
 
 
 def log(msg):
@@ -89,8 +91,12 @@ def hbm_probes(nbytes: int, reps: int = 3) -> dict:
 
 
 def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the decode kernels' sources, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(key: str = "global_main"):
@@ -371,6 +377,38 @@ def main():
         "speedup_vs_stored_keys": round(gl_ms / ms, 3) if ms else None,
         "main_kernel_hbm_traffic": read_traffic("kfv_main"),
     }
+    log("prefill / chunked prefill (MFMA-bound; algorithmic flops of the unmasked pairs)")
+    pre = {}
+    for name in sorted(synth.PREFILL_WORKLOADS):
+        pc = synth.make_prefill_workload(name, seed=args.seed, device=dev, fill=0.0)
+        fn = gqa.gqa_prefill_sliding if pc.variant == "sliding" else gqa.gqa_prefill_global
+        o_pf = torch.empty_like(pc.q)
+
+        def pf_call():
+            fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
+               stream=stream)
+
+        for _ in range(2):
+            pf_call()
+        reps = 5
+        gqa.profile_begin(reps + 2)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        for _ in range(reps):
+            pf_call()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        pprof = gqa.profile_read()[(pc.variant, "prefill")]
+        ms = a_ev.elapsed_time(b_ev) / reps
+        fl = pc.flops()
+        pre[name] = {"B": pc.B, "query_rows": pc.N, "seq_len": int(pc.seq_lens[0]),
+                     "cache": "paged16" if pc.block_table is not None else "contiguous",
+                     "us_per_call": round(ms * 1e3, 1),
+                     "kernel_us": round(pprof[1] / max(pprof[0], 1) * 1e3, 1),
+                     "flops_per_call": fl, "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pc, o_pf
+    line["config"]["prefill"] = pre
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
     line["roofline"]["measured_read_stream_GBps"] = probes["read_GBps"]

@@ -7,7 +7,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCE = os.path.join(PKG, "csrc", "gqa_decode.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, "gqa_decode.hip"), os.path.join(CSRC, "gqa_prefill.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgqadecode.so")
 ARCH = "gfx950"
@@ -32,7 +33,7 @@ def flags() -> list[str]:
 def build(verbose: bool = False) -> str:
     """Always recompiles; returns the library path."""
     tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *flags(), SOURCE, "-o", tmp]
+    cmd = [hipcc(), *flags(), *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(x for x in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in x)

@@ -1,0 +1,476 @@
+// gqa_prefill.hip -- gfx950 prefill / chunked-prefill attention for the
+// Gemma-4-31B text decoder (both attention geometries of the decode kernels,
+// with the causal and sliding masks of the architecture page's compact
+// forward pass).  The C ABI is declared in include/gqa_decode.h.
+
+#include "gqa_common.h"
+
+namespace {
+
+// ----------------------------------------------------------------- prefill
+// Attention of a chunk of new tokens per sequence (prefill / chunked prefill),
+// the chunk's K/V rows already in the cache: query row n of sequence b
+// (cu_q[b] <= n < cu_q[b+1], T_b rows) sits at position p = L_b - T_b + t and
+// attends to the keys its mask keeps (global: s <= p; sliding: p - W < s <= p).
+//
+// Work: the query rows of one (sequence, kv head g) form T_b*G columns
+// (token-major, the G heads of a token adjacent); a wave takes 16 of them, a
+// work-group 64.  The work-group walks the union of its columns' key ranges
+// in steps of PT positions (32 for bf16, two 16-key MFMA halves; 16 for f32):
+// each K/V step is fetched once with coalesced 16-byte loads into a
+// double-buffered LDS tile with rows padded by 16 bytes (the 16 rows one lane
+// group reads fall in distinct banks, and every operand address is a lane
+// base plus an immediate), which all four waves use with every MFMA column
+// masked to its own range.  bf16 P@V runs on 16x16x32 MFMAs over both halves
+// of a step.  Work-groups of one (b, g) are placed on one XCD so their shared
+// tiles stay in that XCD's L2.
+
+struct PrefillArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  char* o;
+  int32_t B, N, cap, max_pages, num_pages, window;
+};
+
+constexpr int kPrefillCols = 16;                  // query columns per wave
+constexpr int kPrefillColsPerWg = kPrefillCols * kWaves;
+constexpr int kXcds = 8;
+
+template <int KV, bool BF16>
+constexpr int prefill_waves_per_simd() {
+  return (KV == 16 && BF16) ? 2 : 1;
+}
+
+template <int KV, int D, bool PAGED, bool BF16>
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) void gqa_prefill_kernel(
+    PrefillArgs a) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
+                VBLK = Gm::VBLK;
+  constexpr size_t POS = Gm::POS;
+  constexpr int PT = BF16 ? 32 : 16;                // key positions per step
+  constexpr int NH = PT / 16;                       // 16-key halves per step
+  constexpr int RS = ROW + 16;                      // padded LDS row stride
+  constexpr int TILE_BYTES = PT * RS;               // one K (or V) step in LDS
+  constexpr int LDPT = 2 * PT * NCH / kThreads;     // 16-byte chunks per thread per step
+  static_assert(LDPT * kThreads == 2 * PT * NCH, "step split");
+  static_assert(NCH >= 64 || (kThreads % NCH) == 0, "rows per fetch instruction");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int g = blockIdx.y;
+
+  // ---- work-groups per sequence (ceil(T_b*G / 64)) and their prefix, in LDS
+  __shared__ int s_wg0[kMaxBatch + 1];
+  __shared__ int s_cu[kMaxBatch + 1];
+  __shared__ int s_len[kMaxBatch];
+  __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE_BYTES];  // [buffer][K, V]
+  if (threadIdx.x < 64) {
+    int cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      cnt[i] = 0;
+      if (b < a.B) {
+        const int c0 = a.cu_q[b], c1 = a.cu_q[b + 1];
+        const int T = c1 > c0 ? c1 - c0 : 0;
+        cnt[i] = (T * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg;
+        s_cu[b] = c0;
+        s_len[b] = a.seq_lens[b];
+        if (b == a.B - 1) s_cu[a.B] = c1;
+      }
+    }
+    const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    int incl = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int run_b = incl - lsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      if (b < a.B) s_wg0[b] = run_b;
+      run_b += cnt[i];
+    }
+    if (lane == 63) s_wg0[a.B] = incl;
+  }
+  __syncthreads();
+  // XCD-aware order: the hardware deals work-groups round-robin over the XCDs,
+  // so consecutive logical work-groups (same (b, g), neighbouring columns)
+  // are given block ids that land on one XCD (gridDim.x is a multiple of 8)
+  const int wg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (wg >= s_wg0[a.B]) return;  // the whole work-group leaves together
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = a.B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (s_wg0[mid] <= wg) lo_b = mid;
+      else hi_b = mid - 1;
+    }
+    b = lo_b;
+  }
+  const int cu = s_cu[b];
+  const int T = s_cu[b + 1] - cu;
+  const int cols = T * G;
+  const int L = min(s_len[b], a.cap);  // clamped for memory safety
+  const int wcol0 = (wg - s_wg0[b]) * kPrefillColsPerWg;  // < cols
+  const int col0 = wcol0 + wave * kPrefillCols;
+  const bool wave_live = col0 < cols;  // dead waves still take part in the barriers
+
+  // ---- this lane's column (n = r): token, head, position, key range
+  const int col = col0 + r;
+  const bool live = col < cols;
+  const int cl = live ? col : cols - 1;
+  const int t_n = cl / G;
+  const int head = g * G + cl % G;
+  const int p_n = L - T + t_n;
+  const int lo_n = a.window > 0 ? max(0, p_n - a.window + 1) : 0;
+  // the work-group's key range: the union over its columns (token-major)
+  const int wcol_end = min(wcol0 + kPrefillColsPerWg, cols);
+  const int p_last = L - T + (wcol_end - 1) / G;
+  const int p_first = max(L - T + wcol0 / G, 0);
+  const int range_lo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
+  const int range_hi = p_last;  // inclusive
+
+  WaveState<KV, D, BF16> st;
+#pragma unroll
+  for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  if (range_hi >= 0) {
+    // ---- the lane's query operands: column r, chunks 4c+j (bf16: registers;
+    // f32, a parity case, reads them from global memory at every step)
+    u32x4 qreg[BF16 ? KCH : 1];
+    const char* qsrc = a.q + ((size_t)(cu + t_n) * kHeads + head) * ROW;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c)
+        qreg[c] = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+    const int last_page = range_hi / kPage;
+
+    // ---- cooperative step fetch.  Rows are clamped into the range (every step
+    // lies within [range_lo & ~(PT-1), range_hi], so a clamped row stays in
+    // the step's pages).  Rows of at least 1 KiB go straight to LDS (one
+    // 16-byte-per-lane LDS-DMA load per KiB: LDS address = base + 16*lane, all
+    // other addressing wave-uniform); shorter rows go through registers
+    // (thread t takes chunks t + 256u of the K+V step).
+    constexpr bool DMA = ROW % 1024 == 0;
+    constexpr int IPR = DMA ? ROW / 1024 : 1;       // DMA loads per row
+    constexpr int DMA_PER_WAVE = 2 * PT * IPR / kWaves;
+    u32x4 ld[DMA ? 1 : LDPT];
+    auto fetch = [&](int step, int& okbits, int buf) {
+      const int pos0 = step * PT;
+      size_t base[NH];
+      okbits = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        if constexpr (PAGED) {
+          const int pi = pos0 / kPage + h;
+          const int page = pi <= last_page ? bt[pi] : 0;
+          const bool ok = page >= 0 && page < a.num_pages;
+          okbits |= ok ? (1 << h) : 0;
+          base[h] = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+        } else {
+          okbits |= 1 << h;
+          base[h] = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
+        }
+      }
+      if constexpr (DMA) {
+#pragma unroll
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+          const int inst = wave + kWaves * i;  // wave-uniform
+          const int which = inst / (PT * IPR);
+          const int row = (inst / IPR) % PT;
+          const int part = inst % IPR;
+          const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;
+          const int h = rel >> 4;
+          const size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
+                             (size_t)(rel & 15) * POS + part * 1024;
+          __builtin_amdgcn_global_load_lds(
+              (const void*)((which ? a.v : a.k) + off + lane * 16),
+              (__attribute__((address_space(3))) void*)&s_kv[buf][which][row * RS + part * 1024],
+              16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < LDPT; ++u) {
+          const int q = threadIdx.x + kThreads * u;
+          const int which = q / (PT * NCH);  // 0: K, 1: V
+          const int row = (q / NCH) % PT;
+          const int c = q % NCH;
+          const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
+          const int h = rel >> 4;
+          size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
+                       (size_t)(rel & 15) * POS + c * 16;
+          ld[u] = load16((which ? a.v : a.k) + off);
+        }
+      }
+    };
+    auto stash = [&](int buf) {
+      if constexpr (!DMA) {
+#pragma unroll
+        for (int u = 0; u < LDPT; ++u) {
+          const int q = threadIdx.x + kThreads * u;
+          const int which = q / (PT * NCH);
+          const int row = (q / NCH) % PT;
+          const int c = q % NCH;
+          *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * RS + c * 16]) = ld[u];
+        }
+      } else {
+        // the step's LDS-DMA loads have landed before the barrier that follows
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    };
+
+    const int step_begin = range_lo / PT, step_end = range_hi / PT;  // inclusive
+    int ok_cur, ok_nxt = 0;
+    fetch(step_begin, ok_cur, 0);
+    stash(0);
+    __syncthreads();
+    const int kbase = r * RS + j * 16;             // key operand: row r (+16h), chunk 4c+j
+    const int vbase = 4 * j * RS + r * 16;         // value operand: rows 4j+i (+16h), chunk r+16blk
+    for (int step = step_begin; step <= step_end; ++step) {
+      const int buf = (step - step_begin) & 1;
+      const bool more = step < step_end;
+      if (more) fetch(step + 1, ok_nxt, buf ^ 1);
+      if (wave_live) {
+        const char* kt = s_kv[buf][0] + kbase;
+        const char* vt = s_kv[buf][1] + vbase;
+        // logits z[h][key 16h+4j+i][column r]
+        f32x4 z[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+          const char* kh = kt + h * 16 * RS;
+          if constexpr (BF16) {
+#pragma unroll
+            for (int c = 0; c < KCH; c += 2) {
+              const u32x4 k0 = *reinterpret_cast<const u32x4*>(kh + c * 64);
+              const u32x4 k1 = *reinterpret_cast<const u32x4*>(kh + c * 64 + 64);
+              z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0),
+                                                           __builtin_bit_cast(bf16x8, qreg[c]), z0,
+                                                           0, 0, 0);
+              z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1),
+                                                           __builtin_bit_cast(bf16x8, qreg[c + 1]),
+                                                           z1, 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+              const u32x4 kc = *reinterpret_cast<const u32x4*>(kh + c * 64);
+              const u32x4 qc = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+              for (int e = 0; e < 4; e += 2) {
+                z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e), chunk_f32(qc, e), z0,
+                                                          0, 0, 0);
+                z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e + 1),
+                                                          chunk_f32(qc, e + 1), z1, 0, 0, 0);
+              }
+            }
+          }
+          z[h] = z0 + z1;
+        }
+        // each column keeps the keys of its own mask
+        const int pos0 = step * PT;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = pos0 + 16 * h + 4 * j + i;
+            if (!(((ok_cur >> h) & 1) && live && s >= lo_n && s <= p_n)) z[h][i] = -INFINITY;
+            tmax = fmaxf(tmax, z[h][i]);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool grow = tmax > st.m + kRescaleGap;
+        if (__any(grow)) {
+          const float m_next = grow ? tmax : st.m;
+          const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+          if (grow) {
+            st.l *= alpha;
+#pragma unroll
+            for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+              for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
+          }
+          st.m = m_next;
+        }
+        const float m_use = st.m == -INFINITY ? 0.f : st.m;
+        float p[NH][4];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast((z[h][i] - m_use) * kLog2e);
+        if constexpr (BF16) {
+          // P^T operand: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
+          u32x4 pt;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            pt[2 * h] = bf16_pack2(p[h][0], p[h][1]);
+            pt[2 * h + 1] = bf16_pack2(p[h][2], p[h][3]);
+            st.l += (bf16_value(pt[2 * h] & 0xffffu) + bf16_value(pt[2 * h] >> 16)) +
+                    (bf16_value(pt[2 * h + 1] & 0xffffu) + bf16_value(pt[2 * h + 1] >> 16));
+          }
+#pragma unroll
+          for (int blk = 0; blk < VBLK; ++blk) {
+            u32x4 vr[2][4];  // value rows 16h+4j+i, chunk r+16*blk
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                vr[h][i] = *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RS + blk * 256);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+              const int dw = e >> 1;
+              u32x4 vtr;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                vtr[2 * h] = __builtin_amdgcn_perm(vr[h][1][dw], vr[h][0][dw], sel);
+                vtr[2 * h + 1] = __builtin_amdgcn_perm(vr[h][3][dw], vr[h][2][dw], sel);
+              }
+              st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, vtr), __builtin_bit_cast(bf16x8, pt), st.acc[blk][e],
+                  0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            st.l += (p[h][0] + p[h][1]) + (p[h][2] + p[h][3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int blk = 0; blk < VBLK; ++blk) {
+                const u32x4 vc =
+                    *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RS + blk * 256);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vc, e), p[h][i],
+                                                                        st.acc[blk][e], 0, 0, 0);
+              }
+          }
+        }
+      }
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+      ok_cur = ok_nxt;
+    }
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+  }
+  if (live) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;  // a column before position 0: zero row
+    store_o<KV, D, BF16>(st, a.o + ((size_t)(cu + t_n) * kHeads + head) * ROW, inv);
+  }
+}
+
+typedef void (*PrefillFn)(PrefillArgs);
+
+template <int KV, int D>
+PrefillFn pick_prefill(bool paged, bool bf16) {
+  if (paged)
+    return bf16 ? gqa_prefill_kernel<KV, D, true, true> : gqa_prefill_kernel<KV, D, true, false>;
+  return bf16 ? gqa_prefill_kernel<KV, D, false, true> : gqa_prefill_kernel<KV, D, false, false>;
+}
+
+constexpr int kMaxPrefillRows = 1 << 24;  // query rows per call
+constexpr int kProfPrefill = 9;           // profiling kinds 9 (sliding), 10 (global)
+
+int run_prefill(int variant, bool paged, const void* q, const void* k, const void* v,
+                const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                int32_t num_pages, int32_t dtype, void* stream_) {
+  if (!q || !k || !v || !cu_q || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
+  VariantInfo vi;
+  if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
+  if (B < 1 || B > kMaxBatch || N < 1 || N > kMaxPrefillRows) return GQA_ERR_SHAPE;
+  int cap;
+  if (paged) {
+    if (max_pages < 1 || max_pages > kMaxSeq / kPage || num_pages < 1) return GQA_ERR_SHAPE;
+    cap = max_pages * kPage;
+  } else {
+    if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
+    cap = S_max;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGN;
+  PrefillArgs pa;
+  pa.q = static_cast<const char*>(q);
+  pa.k = static_cast<const char*>(k);
+  pa.v = static_cast<const char*>(v);
+  pa.cu_q = cu_q;
+  pa.seq_lens = seq_lens;
+  pa.block_table = block_table;
+  pa.o = static_cast<char*>(o);
+  pa.B = B;
+  pa.N = N;
+  pa.cap = cap;
+  pa.max_pages = paged ? max_pages : 0;
+  pa.num_pages = paged ? num_pages : 0;
+  pa.window = vi.window;
+  const bool bf16 = dtype == GQA_BF16;
+  PrefillFn fn = variant == GQA_SLIDING ? pick_prefill<16, 256>(paged, bf16)
+                                        : pick_prefill<4, 512>(paged, bf16);
+  // an upper bound of the work-groups sum_b ceil(T_b*G/64): the rest exit at once
+  const int G = kHeads / vi.KV;
+  int64_t n_wg = ((int64_t)N * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg + B;
+  n_wg = (n_wg + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD remap needs a multiple of 8
+  const unsigned grid_x = (unsigned)n_wg;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int slot = gqa_detail::prof_begin(kProfPrefill + variant, stream);
+  hipLaunchKernelGGL(fn, dim3(grid_x, (unsigned)vi.KV), dim3(kThreads), 0, stream, pa);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  gqa_detail::prof_end(slot, stream);
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_prefill_sliding(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                        const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                        int32_t dtype, void* stream) {
+  return run_prefill(GQA_SLIDING, false, q, k, v, nullptr, 0, cu_q, seq_lens, o, B, N, S_max, 0,
+                     dtype, stream);
+}
+
+int gqa_prefill_global(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                       const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
+                       int32_t dtype, void* stream) {
+  return run_prefill(GQA_GLOBAL, false, q, k, v, nullptr, 0, cu_q, seq_lens, o, B, N, S_max, 0,
+                     dtype, stream);
+}
+
+int gqa_prefill_sliding_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                              const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                              int32_t num_pages, int32_t dtype, void* stream) {
+  return run_prefill(GQA_SLIDING, true, q, k_pool, v_pool, block_table, max_pages, cu_q,
+                     seq_lens, o, B, N, 0, num_pages, dtype, stream);
+}
+
+int gqa_prefill_global_paged(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                             const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                             int32_t num_pages, int32_t dtype, void* stream) {
+  return run_prefill(GQA_GLOBAL, true, q, k_pool, v_pool, block_table, max_pages, cu_q, seq_lens,
+                     o, B, N, 0, num_pages, dtype, stream);
+}
+
+}  // extern "C"
