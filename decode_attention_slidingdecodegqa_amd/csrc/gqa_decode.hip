@@ -338,21 +338,24 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
             vb[e] = chunk_f32(src[t + TP], e);
           }
         }
-        // four pairs at a time: the scheduler barrier bounds the LDS reads in
-        // flight (registers are the scarce resource of this kernel)
+        // the table entries of the E pairs first, all reads in flight, then the
+        // math (interleaving them serialises the LDS latency)
+        f32x4 Mt[E];
+        f32x4 Bt[E / 2];
 #pragma unroll
-        for (int e0 = 0; e0 < E; e0 += 4) {
+        for (int e = 0; e < E; ++e)
+          Mt[e] = *reinterpret_cast<const f32x4*>(rl->m[E * (4 * t + j) + e][rr]);
 #pragma unroll
-          for (int e = e0; e < e0 + 4; ++e) {
-            const int i = E * (4 * t + j) + e;  // pair index
-            const f32x4 M = *reinterpret_cast<const f32x4*>(rl->m[i][rr]);
-            const f32x2 Bs = *reinterpret_cast<const f32x2*>(rl->base[wave][i]);
-            const float xa = M[0] * va[e] + M[1] * vb[e];
-            const float xb = M[2] * va[e] + M[3] * vb[e];
-            va[e] = Bs[0] * xa - Bs[1] * xb;
-            vb[e] = Bs[1] * xa + Bs[0] * xb;
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < E; e += 2)
+          Bt[e / 2] = *reinterpret_cast<const f32x4*>(rl->base[wave][E * (4 * t + j) + e]);
+        #pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const f32x4 M = Mt[e];
+          const float bc = Bt[e / 2][2 * (e & 1)], bs = Bt[e / 2][2 * (e & 1) + 1];
+          const float xa = M[0] * va[e] + M[1] * vb[e];
+          const float xb = M[2] * va[e] + M[3] * vb[e];
+          va[e] = bc * xa - bs * xb;
+          vb[e] = bs * xa + bc * xb;
         }
         u32x4 ka, kb;
         if constexpr (BF16) {
