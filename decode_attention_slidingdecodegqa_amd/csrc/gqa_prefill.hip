@@ -36,13 +36,26 @@ struct PrefillArgs {
   int32_t B, N, cap, max_pages, num_pages, window;
 };
 
-constexpr int kPrefillCols = 16;                  // query columns per wave
-constexpr int kPrefillColsPerWg = kPrefillCols * kWaves;
 constexpr int kXcds = 8;
+
+// 16-column MFMA blocks per wave.  Two blocks would let every K/V operand read
+// from LDS feed two MFMAs, but they need one wave per SIMD; measured on the
+// sliding kernel, two waves per SIMD with one block each hide more latency
+// (1172 us against 1501 us on 8 x 2048 tokens), so every variant runs one.
+template <int KV, bool BF16>
+constexpr int prefill_col_blocks() {
+  return 1;
+}
 
 template <int KV, bool BF16>
 constexpr int prefill_waves_per_simd() {
   return (KV == 16 && BF16) ? 2 : 1;
+}
+
+// query columns per work-group (four waves)
+template <int KV, bool BF16>
+constexpr int prefill_cols_per_wg() {
+  return 16 * prefill_col_blocks<KV, BF16>() * kWaves;
 }
 
 template <int KV, int D, bool PAGED, bool BF16>
@@ -52,6 +65,8 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
                 VBLK = Gm::VBLK;
   constexpr size_t POS = Gm::POS;
+  constexpr int CB = prefill_col_blocks<KV, BF16>();
+  constexpr int CPW = prefill_cols_per_wg<KV, BF16>();  // columns per work-group
   constexpr int PT = BF16 ? 32 : 16;                // key positions per step
   constexpr int NH = PT / 16;                       // 16-key halves per step
   constexpr int RS = ROW + 16;                      // padded LDS row stride
@@ -60,7 +75,9 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   static_assert(LDPT * kThreads == 2 * PT * NCH, "step split");
   static_assert(NCH >= 64 || (kThreads % NCH) == 0, "rows per fetch instruction");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values go through readfirstlane so that the address math of
+  // the tile fetch runs on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
   const int g = blockIdx.y;
@@ -79,7 +96,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       if (b < a.B) {
         const int c0 = a.cu_q[b], c1 = a.cu_q[b + 1];
         const int T = c1 > c0 ? c1 - c0 : 0;
-        cnt[i] = (T * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg;
+        cnt[i] = (T * G + CPW - 1) / CPW;
         s_cu[b] = c0;
         s_len[b] = a.seq_lens[b];
         if (b == a.B - 1) s_cu[a.B] = c1;
@@ -115,48 +132,60 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       if (s_wg0[mid] <= wg) lo_b = mid;
       else hi_b = mid - 1;
     }
-    b = lo_b;
+    b = __builtin_amdgcn_readfirstlane(lo_b);
   }
-  const int cu = s_cu[b];
-  const int T = s_cu[b + 1] - cu;
+  const int cu = __builtin_amdgcn_readfirstlane(s_cu[b]);
+  const int T = __builtin_amdgcn_readfirstlane(s_cu[b + 1]) - cu;
   const int cols = T * G;
-  const int L = min(s_len[b], a.cap);  // clamped for memory safety
-  const int wcol0 = (wg - s_wg0[b]) * kPrefillColsPerWg;  // < cols
-  const int col0 = wcol0 + wave * kPrefillCols;
+  const int L = min(__builtin_amdgcn_readfirstlane(s_len[b]), a.cap);  // clamped for memory safety
+  const int wcol0 = (wg - s_wg0[b]) * CPW;  // < cols
+  const int col0 = wcol0 + wave * 16 * CB;
   const bool wave_live = col0 < cols;  // dead waves still take part in the barriers
 
-  // ---- this lane's column (n = r): token, head, position, key range
-  const int col = col0 + r;
-  const bool live = col < cols;
-  const int cl = live ? col : cols - 1;
-  const int t_n = cl / G;
-  const int head = g * G + cl % G;
-  const int p_n = L - T + t_n;
-  const int lo_n = a.window > 0 ? max(0, p_n - a.window + 1) : 0;
+  // ---- this lane's column r of each block: token, head, position, key range
+  bool live[CB];
+  int t_n[CB], head[CB], p_n[CB], lo_n[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = col0 + 16 * cb + r;
+    live[cb] = col < cols;
+    const int cl = live[cb] ? col : cols - 1;
+    t_n[cb] = cl / G;
+    head[cb] = g * G + cl % G;
+    p_n[cb] = L - T + t_n[cb];
+    lo_n[cb] = a.window > 0 ? max(0, p_n[cb] - a.window + 1) : 0;
+  }
   // the work-group's key range: the union over its columns (token-major)
-  const int wcol_end = min(wcol0 + kPrefillColsPerWg, cols);
+  const int wcol_end = min(wcol0 + CPW, cols);
   const int p_last = L - T + (wcol_end - 1) / G;
   const int p_first = max(L - T + wcol0 / G, 0);
   const int range_lo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
   const int range_hi = p_last;  // inclusive
 
-  WaveState<KV, D, BF16> st;
+  WaveState<KV, D, BF16> st[CB];
 #pragma unroll
-  for (int blk = 0; blk < VBLK; ++blk)
+  for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
+    for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+      for (int e = 0; e < E; ++e) st[cb].acc[blk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st[cb].m = -INFINITY;
+    st[cb].l = 0.f;
+  }
 
   if (range_hi >= 0) {
     // ---- the lane's query operands: column r, chunks 4c+j (bf16: registers;
     // f32, a parity case, reads them from global memory at every step)
-    u32x4 qreg[BF16 ? KCH : 1];
-    const char* qsrc = a.q + ((size_t)(cu + t_n) * kHeads + head) * ROW;
-    if constexpr (BF16) {
+    u32x4 qreg[CB][BF16 ? KCH : 1];
+    const char* qsrc[CB];
 #pragma unroll
-      for (int c = 0; c < KCH; ++c)
-        qreg[c] = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int cb = 0; cb < CB; ++cb) {
+      qsrc[cb] = a.q + ((size_t)(cu + t_n[cb]) * kHeads + head[cb]) * ROW;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+          qreg[cb][c] = live[cb] ? load16(qsrc[cb] + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
     const int last_page = range_hi / kPage;
@@ -171,6 +200,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
     constexpr int IPR = DMA ? ROW / 1024 : 1;       // DMA loads per row
     constexpr int DMA_PER_WAVE = 2 * PT * IPR / kWaves;
     u32x4 ld[DMA ? 1 : LDPT];
+    // register path: thread t stages chunk t % NCH of rows t / NCH + (256/NCH)*u
+    const int ld_row0 = threadIdx.x / NCH;
+    const int ld_c = threadIdx.x % NCH;
+    static_assert(DMA || (kThreads / NCH <= 16 && 16 % (kThreads / NCH) == 0),
+                  "register staging: a thread's rows stay within one 16-row half");
     auto fetch = [&](int step, int& okbits, int buf) {
       const int pos0 = step * PT;
       size_t base[NH];
@@ -204,6 +238,18 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
               (__attribute__((address_space(3))) void*)&s_kv[buf][which][row * RS + part * 1024],
               16, 0, 0);
         }
+      } else if (pos0 >= range_lo && pos0 + PT - 1 <= range_hi) {
+        // an interior step needs no clamp: row, K/V and page half of chunk u
+        // are compile-time offsets from the thread's (row0, column chunk)
+#pragma unroll
+        for (int u = 0; u < LDPT; ++u) {
+          constexpr int RPU = kThreads / NCH;             // rows per u
+          const int which = (RPU * u) / PT;               // 0: K, 1: V
+          const int rin = (RPU * u) % PT;                 // + row0 < 16 within its half
+          const int h = rin / 16;
+          const size_t off = base[NH == 1 ? 0 : h] + (size_t)(ld_row0 + rin % 16) * POS + ld_c * 16;
+          ld[u] = load16((which ? a.v : a.k) + off);
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < LDPT; ++u) {
@@ -223,11 +269,10 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       if constexpr (!DMA) {
 #pragma unroll
         for (int u = 0; u < LDPT; ++u) {
-          const int q = threadIdx.x + kThreads * u;
-          const int which = q / (PT * NCH);
-          const int row = (q / NCH) % PT;
-          const int c = q % NCH;
-          *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * RS + c * 16]) = ld[u];
+          constexpr int RPU = kThreads / NCH;
+          const int which = (RPU * u) / PT;
+          const int row = ld_row0 + (RPU * u) % PT;
+          *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * RS + ld_c * 16]) = ld[u];
         }
       } else {
         // the step's LDS-DMA loads have landed before the barrier that follows
@@ -249,82 +294,100 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       if (wave_live) {
         const char* kt = s_kv[buf][0] + kbase;
         const char* vt = s_kv[buf][1] + vbase;
-        // logits z[h][key 16h+4j+i][column r]
-        f32x4 z[NH];
+        // logits z[cb][h][key 16h+4j+i][column r of block cb]; each K operand
+        // read from LDS feeds the MFMAs of every column block
+        f32x4 z[CB][NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+          f32x4 z0[CB], z1[CB];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            z0[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            z1[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
           const char* kh = kt + h * 16 * RS;
           if constexpr (BF16) {
 #pragma unroll
             for (int c = 0; c < KCH; c += 2) {
-              const u32x4 k0 = *reinterpret_cast<const u32x4*>(kh + c * 64);
-              const u32x4 k1 = *reinterpret_cast<const u32x4*>(kh + c * 64 + 64);
-              z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0),
-                                                           __builtin_bit_cast(bf16x8, qreg[c]), z0,
-                                                           0, 0, 0);
-              z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1),
-                                                           __builtin_bit_cast(bf16x8, qreg[c + 1]),
-                                                           z1, 0, 0, 0);
+              const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + c * 64));
+              const bf16x8 k1 =
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + c * 64 + 64));
+#pragma unroll
+              for (int cb = 0; cb < CB; ++cb) {
+                z0[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    k0, __builtin_bit_cast(bf16x8, qreg[cb][c]), z0[cb], 0, 0, 0);
+                z1[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    k1, __builtin_bit_cast(bf16x8, qreg[cb][c + 1]), z1[cb], 0, 0, 0);
+              }
             }
           } else {
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
               const u32x4 kc = *reinterpret_cast<const u32x4*>(kh + c * 64);
-              const u32x4 qc = live ? load16(qsrc + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+              const u32x4 qc =
+                  live[0] ? load16(qsrc[0] + (4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
               for (int e = 0; e < 4; e += 2) {
-                z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e), chunk_f32(qc, e), z0,
-                                                          0, 0, 0);
-                z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e + 1),
-                                                          chunk_f32(qc, e + 1), z1, 0, 0, 0);
+                z0[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e), chunk_f32(qc, e),
+                                                             z0[0], 0, 0, 0);
+                z1[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kc, e + 1),
+                                                             chunk_f32(qc, e + 1), z1[0], 0, 0, 0);
               }
             }
           }
-          z[h] = z0 + z1;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) z[cb][h] = z0[cb] + z1[cb];
         }
-        // each column keeps the keys of its own mask
+        // each column keeps the keys of its own mask; online softmax per block
         const int pos0 = step * PT;
-        float tmax = -INFINITY;
+        float p[CB][NH][4];
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
+        for (int cb = 0; cb < CB; ++cb) {
+          WaveState<KV, D, BF16>& sc = st[cb];
+          float tmax = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s = pos0 + 16 * h + 4 * j + i;
-            if (!(((ok_cur >> h) & 1) && live && s >= lo_n && s <= p_n)) z[h][i] = -INFINITY;
-            tmax = fmaxf(tmax, z[h][i]);
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int s_ = pos0 + 16 * h + 4 * j + i;
+              if (!(((ok_cur >> h) & 1) && live[cb] && s_ >= lo_n[cb] && s_ <= p_n[cb]))
+                z[cb][h][i] = -INFINITY;
+              tmax = fmaxf(tmax, z[cb][h][i]);
+            }
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+          const bool grow = tmax > sc.m + kRescaleGap;
+          if (__any(grow)) {
+            const float m_next = grow ? tmax : sc.m;
+            const float alpha = exp2_fast((sc.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
+            if (grow) {
+              sc.l *= alpha;
+#pragma unroll
+              for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+                for (int e = 0; e < E; ++e) sc.acc[blk][e] *= alpha;
+            }
+            sc.m = m_next;
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const bool grow = tmax > st.m + kRescaleGap;
-        if (__any(grow)) {
-          const float m_next = grow ? tmax : st.m;
-          const float alpha = exp2_fast((st.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
-          if (grow) {
-            st.l *= alpha;
+          const float m_use = sc.m == -INFINITY ? 0.f : sc.m;
 #pragma unroll
-            for (int blk = 0; blk < VBLK; ++blk)
+          for (int h = 0; h < NH; ++h)
 #pragma unroll
-              for (int e = 0; e < E; ++e) st.acc[blk][e] *= alpha;
-          }
-          st.m = m_next;
+            for (int i = 0; i < 4; ++i) p[cb][h][i] = exp2_fast((z[cb][h][i] - m_use) * kLog2e);
         }
-        const float m_use = st.m == -INFINITY ? 0.f : st.m;
-        float p[NH][4];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast((z[h][i] - m_use) * kLog2e);
         if constexpr (BF16) {
-          // P^T operand: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
-          u32x4 pt;
+          // P^T operands: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
+          u32x4 pt[CB];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            pt[2 * h] = bf16_pack2(p[h][0], p[h][1]);
-            pt[2 * h + 1] = bf16_pack2(p[h][2], p[h][3]);
-            st.l += (bf16_value(pt[2 * h] & 0xffffu) + bf16_value(pt[2 * h] >> 16)) +
-                    (bf16_value(pt[2 * h + 1] & 0xffffu) + bf16_value(pt[2 * h + 1] >> 16));
-          }
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              pt[cb][2 * h] = bf16_pack2(p[cb][h][0], p[cb][h][1]);
+              pt[cb][2 * h + 1] = bf16_pack2(p[cb][h][2], p[cb][h][3]);
+              st[cb].l += (bf16_value(pt[cb][2 * h] & 0xffffu) + bf16_value(pt[cb][2 * h] >> 16)) +
+                          (bf16_value(pt[cb][2 * h + 1] & 0xffffu) +
+                           bf16_value(pt[cb][2 * h + 1] >> 16));
+            }
 #pragma unroll
           for (int blk = 0; blk < VBLK; ++blk) {
             u32x4 vr[2][4];  // value rows 16h+4j+i, chunk r+16*blk
@@ -343,15 +406,17 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
                 vtr[2 * h] = __builtin_amdgcn_perm(vr[h][1][dw], vr[h][0][dw], sel);
                 vtr[2 * h + 1] = __builtin_amdgcn_perm(vr[h][3][dw], vr[h][2][dw], sel);
               }
-              st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, vtr), __builtin_bit_cast(bf16x8, pt), st.acc[blk][e],
-                  0, 0, 0);
+#pragma unroll
+              for (int cb = 0; cb < CB; ++cb)
+                st[cb].acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, vtr), __builtin_bit_cast(bf16x8, pt[cb]),
+                    st[cb].acc[blk][e], 0, 0, 0);
             }
           }
         } else {
 #pragma unroll
           for (int h = 0; h < NH; ++h) {
-            st.l += (p[h][0] + p[h][1]) + (p[h][2] + p[h][3]);
+            st[0].l += (p[0][h][0] + p[0][h][1]) + (p[0][h][2] + p[0][h][3]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -360,8 +425,8 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
                     *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RS + blk * 256);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  st.acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(vc, e), p[h][i],
-                                                                        st.acc[blk][e], 0, 0, 0);
+                  st[0].acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                      chunk_f32(vc, e), p[0][h][i], st[0].acc[blk][e], 0, 0, 0);
               }
           }
         }
@@ -370,12 +435,18 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       __syncthreads();
       ok_cur = ok_nxt;
     }
-    st.l += __shfl_xor(st.l, 16);
-    st.l += __shfl_xor(st.l, 32);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      st[cb].l += __shfl_xor(st[cb].l, 16);
+      st[cb].l += __shfl_xor(st[cb].l, 32);
+    }
   }
-  if (live) {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;  // a column before position 0: zero row
-    store_o<KV, D, BF16>(st, a.o + ((size_t)(cu + t_n) * kHeads + head) * ROW, inv);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if (live[cb]) {
+      const float inv = st[cb].l > 0.f ? 1.f / st[cb].l : 0.f;  // before position 0: zero row
+      store_o<KV, D, BF16>(st[cb], a.o + ((size_t)(cu + t_n[cb]) * kHeads + head[cb]) * ROW, inv);
+    }
   }
 }
 
@@ -428,7 +499,10 @@ int run_prefill(int variant, bool paged, const void* q, const void* k, const voi
                                         : pick_prefill<4, 512>(paged, bf16);
   // an upper bound of the work-groups sum_b ceil(T_b*G/64): the rest exit at once
   const int G = kHeads / vi.KV;
-  int64_t n_wg = ((int64_t)N * G + kPrefillColsPerWg - 1) / kPrefillColsPerWg + B;
+  const int cpw = variant == GQA_SLIDING
+                      ? (bf16 ? prefill_cols_per_wg<16, true>() : prefill_cols_per_wg<16, false>())
+                      : (bf16 ? prefill_cols_per_wg<4, true>() : prefill_cols_per_wg<4, false>());
+  int64_t n_wg = ((int64_t)N * G + cpw - 1) / cpw + B;
   n_wg = (n_wg + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD remap needs a multiple of 8
   const unsigned grid_x = (unsigned)n_wg;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
