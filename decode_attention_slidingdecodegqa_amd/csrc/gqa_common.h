@@ -63,10 +63,6 @@ __device__ inline u32x4 load16_stream(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ inline unsigned bf16_bits(float x) {
-  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
-}
-
 // Two floats rounded to bf16 (RNE) and packed, the first in the low half: one
 // v_cvt_pk_bf16_f32.
 __device__ inline unsigned bf16_pack2(float lo, float hi) {

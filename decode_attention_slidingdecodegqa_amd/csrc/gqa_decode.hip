@@ -85,28 +85,6 @@ __device__ inline int wave_of(long t, long T, int W) {
   return (int)(((t + 1) * W - 1) / T);
 }
 
-__device__ inline int pick4(int a0, int a1, int a2, int a3, int i) {
-  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
-}
-
-// Store n consecutive fp32 values as 16-byte output chunks.
-template <bool BF16>
-__device__ inline void store_run(char* dst, const float* v, int n) {
-  if constexpr (BF16) {
-    for (int c = 0; c < n / 8; ++c) {
-      u32x4 w;
-      for (int q = 0; q < 4; ++q)
-        w[q] = bf16_pack2(v[8 * c + 2 * q], v[8 * c + 2 * q + 1]);
-      *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
-    }
-  } else {
-    for (int c = 0; c < n / 4; ++c) {
-      f32x4 w = {v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
-      *reinterpret_cast<f32x4*>(dst + 16 * c) = w;
-    }
-  }
-}
-
 // Waves per SIMD the main kernels are compiled for: the sliding bf16 kernels
 // fit two (<= 256 registers), the others need one.
 template <int KV, bool BF16>
