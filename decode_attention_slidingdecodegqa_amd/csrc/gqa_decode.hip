@@ -20,7 +20,7 @@
 //
 //   Tile.  One wave64 consumes a tile with every query head of the GQA group:
 //   QK^T  v_mfma_f32_16x16x32_bf16 (16x16x4_f32 for f32): A = the 16 key rows,
-//         B = the group's query heads padded to 16 zero columns.  The
+//         B = the group's query heads padded to 16 columns.  The
 //         reduction index may be any permutation of d shared by A and B, so
 //         each lane loads whole 16-byte chunks of one key row straight into
 //         the operand registers.
@@ -143,14 +143,15 @@ __device__ void rope_tables_init(const char* w_k, RopeLds* rl) {
 }
 
 // the calling wave's base rotation of the tile starting at position pos0
+// The angle pos0 * f_i is formed in revolutions in double and reduced to
+// [-1/2, 1/2]; the hardware sine and cosine (v_sin_f32 / v_cos_f32, argument in
+// revolutions, absolute error near 1e-6 on that range) then take it.
 __device__ inline void rope_base(RopeLds* rl, int wave, int pos0) {
   const int i = threadIdx.x & 63;
-  const double ang = (double)pos0 * rl->freq[i];
-  const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
-  float sn, c;
-  sincosf((float)red, &sn, &c);
-  rl->base[wave][i][0] = c;
-  rl->base[wave][i][1] = sn;
+  const double rev = (double)pos0 * rl->freq[i] * 0.15915494309189535;  // / 2 pi
+  const float red = (float)(rev - rint(rev));
+  rl->base[wave][i][0] = __builtin_amdgcn_cosf(red);
+  rl->base[wave][i][1] = __builtin_amdgcn_sinf(red);
 }
 
 // Accumulates into st the tiles k_begin, k_begin + step, ... (< k_end) of unit
@@ -186,9 +187,12 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   if (n_it == 0) return;
 
   // The group's query heads live in the wave's LDS slice (row h = head g*G+h,
-  // NCH chunks); QK^T reads them back per tile as the B operand, columns >= G
-  // being zero.  Their global loads go first and the LDS store waits for the
-  // first tile's K/V loads to be in flight, so the two latencies overlap.
+  // NCH chunks); QK^T reads them back per tile as the B operand.  Columns
+  // >= G of the 16-wide operand are never stored or merged: they are zero, or
+  // repeat head 0 where an unconditional read pays (a select there becomes a
+  // branch around every read).  The global loads go first and the LDS store
+  // waits for the first tile's K/V loads to be in flight, so the two
+  // latencies overlap.
   u32x4 qstage[QPL];
   {
     const char* qsrc = a.q + ((size_t)b * kHeads + g * G) * ROW;
@@ -410,8 +414,11 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       if constexpr (BF16) {
 #pragma unroll
         for (int c = 0; c < KCH; c += 2) {
-          const u32x4 q0 = r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
-          const u32x4 q1 = r < G ? qrow[4 * c + 4 + j] : u32x4{0u, 0u, 0u, 0u};
+          // columns >= G: zero (stored-key kernels, HBM-bound: a branch around
+          // the read costs nothing and the registers are full) or head 0
+          // (keys from values, compute-bound)
+          const u32x4 q0 = KFV || r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 q1 = KFV || r < G ? qrow[4 * c + 4 + j] : u32x4{0u, 0u, 0u, 0u};
           z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c)),
                                                        __builtin_bit_cast(bf16x8, q0), z0, 0, 0, 0);
           z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c + 1)),
@@ -420,7 +427,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       } else {
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-          const u32x4 qc = r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 qc = KFV || r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e), chunk_f32(qc, e), z0,
