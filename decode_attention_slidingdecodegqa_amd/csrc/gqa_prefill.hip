@@ -52,14 +52,24 @@ constexpr int prefill_waves_per_simd() {
   return (KV == 16 && BF16) ? 2 : 1;
 }
 
-// query columns per work-group (four waves)
+// waves per work-group and key positions per step
+template <int KV, bool BF16>
+constexpr int prefill_waves() {
+  return 4;
+}
+template <int KV, bool BF16>
+constexpr int prefill_step() {
+  return BF16 ? 32 : 16;
+}
+
+// query columns per work-group
 template <int KV, bool BF16>
 constexpr int prefill_cols_per_wg() {
-  return 16 * prefill_col_blocks<KV, BF16>() * kWaves;
+  return 16 * prefill_col_blocks<KV, BF16>() * prefill_waves<KV, BF16>();
 }
 
 template <int KV, int D, bool PAGED, bool BF16>
-__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) void gqa_prefill_kernel(
+__global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_per_simd<KV, BF16>())) void gqa_prefill_kernel(
     PrefillArgs a) {
   using Gm = Geo<KV, D, BF16>;
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
@@ -67,13 +77,15 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   constexpr size_t POS = Gm::POS;
   constexpr int CB = prefill_col_blocks<KV, BF16>();
   constexpr int CPW = prefill_cols_per_wg<KV, BF16>();  // columns per work-group
-  constexpr int PT = BF16 ? 32 : 16;                // key positions per step
+  constexpr int PT = prefill_step<KV, BF16>();      // key positions per step
   constexpr int NH = PT / 16;                       // 16-key halves per step
   constexpr int RS = ROW + 16;                      // padded LDS row stride
   constexpr int TILE_BYTES = PT * RS;               // one K (or V) step in LDS
-  constexpr int LDPT = 2 * PT * NCH / kThreads;     // 16-byte chunks per thread per step
-  static_assert(LDPT * kThreads == 2 * PT * NCH, "step split");
-  static_assert(NCH >= 64 || (kThreads % NCH) == 0, "rows per fetch instruction");
+  constexpr int NW = prefill_waves<KV, BF16>();     // waves per work-group
+  constexpr int NT = 64 * NW;                       // threads per work-group
+  constexpr int LDPT = 2 * PT * NCH / NT;           // 16-byte chunks per thread per step
+  static_assert(LDPT * NT == 2 * PT * NCH, "step split");
+  static_assert(NCH >= 64 || (NT % NCH) == 0, "rows per fetch instruction");
   const int lane = threadIdx.x & 63;
   // wave-uniform values go through readfirstlane so that the address math of
   // the tile fetch runs on the scalar unit
@@ -86,7 +98,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
   __shared__ int s_wg0[kMaxBatch + 1];
   __shared__ int s_cu[kMaxBatch + 1];
   __shared__ int s_len[kMaxBatch];
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE_BYTES];  // [buffer][K, V]
+  // two LDS buffers of one step each ([K, V]), separate variables so that the
+  // compiler sees the LDS-DMA into one never aliases the reads of the other
+  // (otherwise it waits for the next step's fetch before reading this one)
+  __shared__ __attribute__((aligned(16))) char s_kv0[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_kv1[2][TILE_BYTES];
   if (threadIdx.x < 64) {
     int cnt[4];
 #pragma unroll
@@ -198,14 +214,14 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
     // (thread t takes chunks t + 256u of the K+V step).
     constexpr bool DMA = ROW % 1024 == 0;
     constexpr int IPR = DMA ? ROW / 1024 : 1;       // DMA loads per row
-    constexpr int DMA_PER_WAVE = 2 * PT * IPR / kWaves;
+    constexpr int DMA_PER_WAVE = 2 * PT * IPR / NW;
     u32x4 ld[DMA ? 1 : LDPT];
     // register path: thread t stages chunk t % NCH of rows t / NCH + (256/NCH)*u
     const int ld_row0 = threadIdx.x / NCH;
     const int ld_c = threadIdx.x % NCH;
-    static_assert(DMA || (kThreads / NCH <= 16 && 16 % (kThreads / NCH) == 0),
+    static_assert(DMA || (NT / NCH <= 16 && 16 % (NT / NCH) == 0),
                   "register staging: a thread's rows stay within one 16-row half");
-    auto fetch = [&](int step, int& okbits, int buf) {
+    auto fetch = [&](int step, int& okbits, auto& dst) {
       const int pos0 = step * PT;
       size_t base[NH];
       okbits = 0;
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       if constexpr (DMA) {
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
-          const int inst = wave + kWaves * i;  // wave-uniform
+          const int inst = wave + NW * i;  // wave-uniform
           const int which = inst / (PT * IPR);
           const int row = (inst / IPR) % PT;
           const int part = inst % IPR;
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
                              (size_t)(rel & 15) * POS + part * 1024;
           __builtin_amdgcn_global_load_lds(
               (const void*)((which ? a.v : a.k) + off + lane * 16),
-              (__attribute__((address_space(3))) void*)&s_kv[buf][which][row * RS + part * 1024],
+              (__attribute__((address_space(3))) void*)&dst[which][row * RS + part * 1024],
               16, 0, 0);
         }
       } else if (pos0 >= range_lo && pos0 + PT - 1 <= range_hi) {
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
         // are compile-time offsets from the thread's (row0, column chunk)
 #pragma unroll
         for (int u = 0; u < LDPT; ++u) {
-          constexpr int RPU = kThreads / NCH;             // rows per u
+          constexpr int RPU = NT / NCH;                   // rows per u
           const int which = (RPU * u) / PT;               // 0: K, 1: V
           const int rin = (RPU * u) % PT;                 // + row0 < 16 within its half
           const int h = rin / 16;
@@ -253,7 +269,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
       } else {
 #pragma unroll
         for (int u = 0; u < LDPT; ++u) {
-          const int q = threadIdx.x + kThreads * u;
+          const int q = threadIdx.x + NT * u;
           const int which = q / (PT * NCH);  // 0: K, 1: V
           const int row = (q / NCH) % PT;
           const int c = q % NCH;
@@ -265,14 +281,14 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
         }
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](auto& dst) {
       if constexpr (!DMA) {
 #pragma unroll
         for (int u = 0; u < LDPT; ++u) {
-          constexpr int RPU = kThreads / NCH;
+          constexpr int RPU = NT / NCH;
           const int which = (RPU * u) / PT;
           const int row = ld_row0 + (RPU * u) % PT;
-          *reinterpret_cast<u32x4*>(&s_kv[buf][which][row * RS + ld_c * 16]) = ld[u];
+          *reinterpret_cast<u32x4*>(&dst[which][row * RS + ld_c * 16]) = ld[u];
         }
       } else {
         // the step's LDS-DMA loads have landed before the barrier that follows
@@ -281,19 +297,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
     };
 
     const int step_begin = range_lo / PT, step_end = range_hi / PT;  // inclusive
-    int ok_cur, ok_nxt = 0;
-    fetch(step_begin, ok_cur, 0);
-    stash(0);
-    __syncthreads();
     const int kbase = r * RS + j * 16;             // key operand: row r (+16h), chunk 4c+j
     const int vbase = 4 * j * RS + r * 16;         // value operand: rows 4j+i (+16h), chunk r+16blk
-    for (int step = step_begin; step <= step_end; ++step) {
-      const int buf = (step - step_begin) & 1;
-      const bool more = step < step_end;
-      if (more) fetch(step + 1, ok_nxt, buf ^ 1);
-      if (wave_live) {
-        const char* kt = s_kv[buf][0] + kbase;
-        const char* vt = s_kv[buf][1] + vbase;
+    auto compute = [&](int step, int ok_cur, auto& cur) {
+        const char* kt = cur[0] + kbase;
+        const char* vt = cur[1] + vbase;
         // logits z[cb][h][key 16h+4j+i][column r of block cb]; each K operand
         // read from LDS feeds the MFMAs of every column block
         f32x4 z[CB][NH];
@@ -430,10 +438,27 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<KV, BF16>())) voi
               }
           }
         }
-      }
-      if (more) stash(buf ^ 1);
+    };
+
+    // one step: fetch the next one into the other buffer, compute on this one,
+    // publish the next (one barrier per step); the loop takes steps in pairs so
+    // that each buffer is named statically
+    int ok_cur, ok_nxt = 0;
+    fetch(step_begin, ok_cur, s_kv0);
+    stash(s_kv0);
+    __syncthreads();
+    auto one_step = [&](int step, auto& cur, auto& nxt) {
+      const bool more = step < step_end;
+      if (more) fetch(step + 1, ok_nxt, nxt);
+      if (wave_live) compute(step, ok_cur, cur);
+      if (more) stash(nxt);
       __syncthreads();
       ok_cur = ok_nxt;
+    };
+    for (int step = step_begin; step <= step_end; step += 2) {
+      one_step(step, s_kv0, s_kv1);
+      if (step + 1 > step_end) break;
+      one_step(step + 1, s_kv1, s_kv0);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -507,7 +532,10 @@ int run_prefill(int variant, bool paged, const void* q, const void* k, const voi
   const unsigned grid_x = (unsigned)n_wg;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const int slot = gqa_detail::prof_begin(kProfPrefill + variant, stream);
-  hipLaunchKernelGGL(fn, dim3(grid_x, (unsigned)vi.KV), dim3(kThreads), 0, stream, pa);
+  const unsigned threads = 64u * (unsigned)(variant == GQA_SLIDING
+                                                ? (bf16 ? prefill_waves<16, true>() : prefill_waves<16, false>())
+                                                : (bf16 ? prefill_waves<4, true>() : prefill_waves<4, false>()));
+  hipLaunchKernelGGL(fn, dim3(grid_x, (unsigned)vi.KV), dim3(threads), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   gqa_detail::prof_end(slot, stream);
   return GQA_OK;

@@ -124,3 +124,41 @@ def test_prefill_workload_sampled(name):
     g = to_f64(got)
     for i, (n, h) in enumerate(rows):
         assert max_err(g[n, h], ref[i]) <= TOL["bf16"], (name, n, h)
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_prefill_many_sequences(variant):
+    # B = 256 sequences (the whole work-group prefix over cu_q), chunks of 0..40
+    # tokens after pasts of 0..1500 positions; sampled rows vs the oracle
+    g = torch.Generator().manual_seed(505)
+    B, cap = 256, 1552
+    q_lens = torch.randint(0, 41, (B,), generator=g)
+    past = torch.randint(0, 1501, (B,), generator=g)
+    lens = (past + q_lens).clamp(max=cap)
+    c = synth.make_prefill_case(variant, "bf16", cap, lens.tolist(), q_lens.tolist(), seed=505,
+                                device="cuda")
+    got = to_f64(hip_prefill(c))
+    assert np.isfinite(got).all()
+    cu = c.cu_q.tolist()
+    for b in (0, 1, 97, 128, 200, 254, 255):
+        T = cu[b + 1] - cu[b]
+        if T == 0:
+            continue
+        # the oracle on this sequence alone (its rows, its cache slice)
+        sub = synth.PrefillCase(c.variant, c.dtype, c.q[cu[b]:cu[b + 1]].cpu(),
+                                c.k[b:b + 1].cpu(), c.v[b:b + 1].cpu(),
+                                torch.tensor([0, T], dtype=torch.int32),
+                                c.seq_lens[b:b + 1].cpu(), None, c.cap, c.window)
+        rows = [(n, h) for n in (0, T - 1) for h in (0, 13, 31)]
+        ref = oracle_prefill(sub, rows=rows)
+        for i, (n, h) in enumerate(rows):
+            assert max_err(got[cu[b] + n, h], ref[i]) <= TOL["bf16"], (b, n, h)
+
+
+def test_prefill_chunk_longer_than_sequence():
+    # outside the domain: rows before position 0 are zero, the rest as defined
+    c = synth.make_prefill_case("sliding", "bf16", 64, [5, 30], [8, 10], seed=506, fill=0.0)
+    got = to_f64(hip_prefill(to_gpu(c)))
+    ref = oracle_prefill(c)
+    assert not got[:3].any()           # tokens 0..2 of sequence 0 sit before position 0
+    assert max_err(got, ref) <= TOL["bf16"]
