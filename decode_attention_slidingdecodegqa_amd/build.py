@@ -30,10 +30,15 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; returns the library path."""
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *flags(), *SOURCES, "-o", tmp]
+# per-source extra flags: the prefill kernels keep their MFMA accumulators in
+# VGPRs (in AGPRs the compiler copies all of them to VGPRs at every key step,
+# for the rarely taken rescale branch)
+SOURCE_FLAGS = {
+    "gqa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(x for x in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in x)
@@ -41,6 +46,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one object per source); returns the library path."""
+    tmp = LIBRARY + ".tmp"
+    common = [f for f in flags() if f != "-shared"]
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(PKG, "_build", os.path.basename(src) + ".o")
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        _run([hipcc(), *common, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src,
+              "-o", obj], verbose)
+        objs.append(obj)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

@@ -47,15 +47,20 @@ constexpr int prefill_col_blocks() {
   return 1;
 }
 
+// bf16: two waves per SIMD (at most 256 VGPRs each; the library builds this
+// file with the MFMA accumulators in VGPRs, so no AGPR is needed)
 template <int KV, bool BF16>
 constexpr int prefill_waves_per_simd() {
-  return (KV == 16 && BF16) ? 2 : 1;
+  return BF16 ? 2 : 1;
 }
 
-// waves per work-group and key positions per step
+// waves per work-group and key positions per step.  Global bf16 runs eight
+// waves (128 columns) on one K/V tile: each fetched step feeds twice the MFMA
+// work of a four-wave group, and the 136 KB double buffer allows only one
+// work-group per CU (4.48 ms against 7.09 ms on 2 x 2048 tokens after 8192).
 template <int KV, bool BF16>
 constexpr int prefill_waves() {
-  return 4;
+  return (KV == 4 && BF16) ? 8 : 4;
 }
 template <int KV, bool BF16>
 constexpr int prefill_step() {
@@ -205,6 +210,10 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     }
     const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
     const int last_page = range_hi / kPage;
+    // block-table entries of 64 consecutive pages, one per lane, refilled when
+    // a step reaches the next 64 (a per-step load of the entry would stall
+    // every step on its latency)
+    int bt_chunk = -1, bt_lane = 0;
 
     // ---- cooperative step fetch.  Rows are clamped into the range (every step
     // lies within [range_lo & ~(PT-1), range_hi], so a clamped row stays in
@@ -229,7 +238,12 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
       for (int h = 0; h < NH; ++h) {
         if constexpr (PAGED) {
           const int pi = pos0 / kPage + h;
-          const int page = pi <= last_page ? bt[pi] : 0;
+          if ((pi >> 6) != bt_chunk) {
+            bt_chunk = pi >> 6;
+            const int e = 64 * bt_chunk + lane;
+            bt_lane = e <= last_page ? bt[e] : 0;
+          }
+          const int page = __builtin_amdgcn_readlane(bt_lane, pi & 63);
           const bool ok = page >= 0 && page < a.num_pages;
           okbits |= ok ? (1 << h) : 0;
           base[h] = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
