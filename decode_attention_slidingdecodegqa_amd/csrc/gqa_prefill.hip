@@ -86,10 +86,12 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
   // padded LDS row strides.  gfx950 serves a 16-byte-per-lane LDS read in
   // groups of 16 lanes that take rows r = 0..7 from one 16-lane quarter and
   // r = 8..15 from the next: the key operand (lane reads row r, chunk j) is
-  // conflict-free with 32 bytes of padding, the value operand (rows 4j + i,
-  // chunk r) with 64 (measured: 16 bytes halve both to ~125 B/clk per CU)
+  // conflict-free with 32 bytes of padding, the f32 value operand (rows
+  // 4j + i, chunk r) with 64, and the bf16 transposing value reads (rows
+  // 4j + r/4, 8 bytes at 8(r%4)) run fastest with 32 (measured: 16 bytes
+  // halve the first two to ~125 B/clk per CU)
   constexpr int RSK = ROW + 32;
-  constexpr int RSV = ROW + 64;
+  constexpr int RSV = BF16 ? ROW + 32 : ROW + 64;
   constexpr int TILE_K = PT * RSK;                  // one K step in LDS
   constexpr int TILE_BYTES = TILE_K + PT * RSV;     // K then V
   constexpr int NW = prefill_waves<KV, BF16>();     // waves per work-group
@@ -191,9 +193,14 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
   const int range_lo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
   const int range_hi = p_last;  // inclusive
 
+  // bf16: acc[blk][e] is the O^T tile t = E*blk + e, lane (r, j) holding
+  // d = 16t + 4j + i of column r; lsum[cb] is the column's sum of weights
+  // (the same on all four lanes of the column), accumulated by an MFMA
   WaveState<KV, D, BF16> st[CB];
+  f32x4 lsum[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
+    lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
@@ -320,7 +327,27 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
 
     const int step_begin = range_lo / PT, step_end = range_hi / PT;  // inclusive
     const int kbase = r * RSK + j * 16;            // key operand: row r (+16h), chunk 4c+j
-    const int vbase = TILE_K + 4 * j * RSV + r * 16;  // value operand: rows 4j+i (+16h), chunk r+16blk
+    // value operand.  bf16: transposing 8-byte reads, lane (r, j) at row
+    // 4j + r/4 (+16 for the second half), d = 16t + 4(r%4); lane (r, j) then
+    // holds V[4j + e][16t + r] (e = 0..3), the A operand of the tile-t MFMA.
+    // f32: rows 4j+i (+16h), chunk r+16blk
+    const int vbase = BF16 ? TILE_K + (4 * j + (r >> 2)) * RSV + 8 * (r & 3)
+                           : TILE_K + 4 * j * RSV + r * 16;
+    // a wave-uniform step that lies inside every column's key range needs no
+    // mask (most steps: the mask only bites on the diagonal and the window edge)
+    int w_lo = lo_n[0], w_hi = p_n[0];
+#pragma unroll
+    for (int cb = 1; cb < CB; ++cb) {
+      w_lo = max(w_lo, lo_n[cb]);
+      w_hi = min(w_hi, p_n[cb]);
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      w_lo = max(w_lo, __shfl_xor(w_lo, d));
+      w_hi = min(w_hi, __shfl_xor(w_hi, d));
+    }
+    w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+    w_hi = __builtin_amdgcn_readfirstlane(w_hi);
     auto compute = [&](int step, int ok_cur, auto& cur) {
         const char* kt = cur + kbase;
         const char* vt = cur + vbase;
@@ -374,24 +401,39 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           WaveState<KV, D, BF16>& sc = st[cb];
+          const bool interior = ok_cur == (1 << NH) - 1 && pos0 >= w_lo && pos0 + PT - 1 <= w_hi;
+          if (!interior) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int s_ = pos0 + 16 * h + 4 * j + i;
+                if (!(((ok_cur >> h) & 1) && live[cb] && s_ >= lo_n[cb] && s_ <= p_n[cb]))
+                  z[cb][h][i] = -INFINITY;
+              }
+          }
           float tmax = -INFINITY;
 #pragma unroll
           for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int s_ = pos0 + 16 * h + 4 * j + i;
-              if (!(((ok_cur >> h) & 1) && live[cb] && s_ >= lo_n[cb] && s_ <= p_n[cb]))
-                z[cb][h][i] = -INFINITY;
-              tmax = fmaxf(tmax, z[cb][h][i]);
-            }
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[cb][h][i]);
+          // the column's max over the four lanes (r, 0..3): lane swaps across
+          // 16-lane rows, then across the 32-lane halves
+          {
+            const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax),
+                                                              __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+            const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                              __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+          }
           const bool grow = tmax > sc.m + kRescaleGap;
           if (__any(grow)) {
             const float m_next = grow ? tmax : sc.m;
             const float alpha = exp2_fast((sc.m - (m_next == -INFINITY ? 0.f : m_next)) * kLog2e);
             if (grow) {
               sc.l *= alpha;
+              lsum[cb] *= alpha;
 #pragma unroll
               for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
@@ -408,40 +450,31 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
         if constexpr (BF16) {
           // P^T operands: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
           u32x4 pt[CB];
+          const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
+          for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               pt[cb][2 * h] = bf16_pack2(p[cb][h][0], p[cb][h][1]);
               pt[cb][2 * h + 1] = bf16_pack2(p[cb][h][2], p[cb][h][3]);
-              st[cb].l += (bf16_value(pt[cb][2 * h] & 0xffffu) + bf16_value(pt[cb][2 * h] >> 16)) +
-                          (bf16_value(pt[cb][2 * h + 1] & 0xffffu) +
-                           bf16_value(pt[cb][2 * h + 1] >> 16));
             }
+            // the column sums of the bf16 weights the P@V MFMAs use
+            lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pt[cb]), lsum[cb], 0,
+                0, 0);
+          }
 #pragma unroll
-          for (int blk = 0; blk < VBLK; ++blk) {
-            u32x4 vr[2][4];  // value rows 16h+4j+i, chunk r+16*blk
+          for (int t = 0; t < D / 16; ++t) {
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vt + 32 * t));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vt + 16 * RSV + 32 * t));
+            const bf16x8 vop =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                vr[h][i] = *reinterpret_cast<const u32x4*>(vt + (16 * h + i) * RSV + blk * 256);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-              const int dw = e >> 1;
-              u32x4 vtr;
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                vtr[2 * h] = __builtin_amdgcn_perm(vr[h][1][dw], vr[h][0][dw], sel);
-                vtr[2 * h + 1] = __builtin_amdgcn_perm(vr[h][3][dw], vr[h][2][dw], sel);
-              }
-#pragma unroll
-              for (int cb = 0; cb < CB; ++cb)
-                st[cb].acc[blk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, vtr), __builtin_bit_cast(bf16x8, pt[cb]),
-                    st[cb].acc[blk][e], 0, 0, 0);
-            }
+            for (int cb = 0; cb < CB; ++cb)
+              st[cb].acc[t / E][t % E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  vop, __builtin_bit_cast(bf16x8, pt[cb]), st[cb].acc[t / E][t % E], 0, 0, 0);
           }
         } else {
 #pragma unroll
@@ -484,15 +517,30 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      st[cb].l += __shfl_xor(st[cb].l, 16);
-      st[cb].l += __shfl_xor(st[cb].l, 32);
+      if constexpr (BF16) {
+        st[cb].l = lsum[cb][0];
+      } else {
+        st[cb].l += __shfl_xor(st[cb].l, 16);
+        st[cb].l += __shfl_xor(st[cb].l, 32);
+      }
     }
   }
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     if (live[cb]) {
       const float inv = st[cb].l > 0.f ? 1.f / st[cb].l : 0.f;  // before position 0: zero row
-      store_o<KV, D, BF16>(st[cb], a.o + ((size_t)(cu + t_n[cb]) * kHeads + head[cb]) * ROW, inv);
+      char* orow = a.o + ((size_t)(cu + t_n[cb]) * kHeads + head[cb]) * ROW;
+      if constexpr (BF16) {
+        // tile t: d = 16t + 4j + [0, 4), 8 bytes per lane
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const f32x4 x = st[cb].acc[t / E][t % E] * inv;
+          *reinterpret_cast<u32x2*>(orow + (16 * t + 4 * j) * 2) =
+              u32x2{bf16_pack2(x[0], x[1]), bf16_pack2(x[2], x[3])};
+        }
+      } else {
+        store_o<KV, D, BF16>(st[cb], orow, inv);
+      }
     }
   }
 }
