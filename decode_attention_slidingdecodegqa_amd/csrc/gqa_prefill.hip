@@ -268,20 +268,45 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
         }
       }
       if constexpr (DMA) {
+        // LDS-DMA through buffer descriptors, one per K/V and 16-row half of
+        // the step, each spanning those 16 rows: the row's offset goes in the
+        // scalar offset and 16*lane in the vector offset, so a load writes
+        // LDS base + 16*lane.  (The flat form of this load makes the compiler
+        // wait for every outstanding LDS read at each use, serialising the
+        // operand reads of the step being computed.)
+        auto dma = [&](int which, int h, int row_in_half, int part, int lds_off) {
+          // the descriptor's base is wave-uniform: keep it in scalar registers
+          const uint64_t addr =
+              (uint64_t)((which ? a.v : a.k) + (NH == 1 || h == 0 ? base[0] : base[NH - 1]));
+          const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+          const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+          const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(((uint64_t)hi << 32) | lo), 0, 16 * (int)POS, 0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsrc, (__attribute__((address_space(3))) void*)&dst[lds_off], 16,
+              lane * 16 + part * 1024, row_in_half * (int)POS, 0, 0);
+        };
+        // interior step (one load per row): wave w loads rows w + NW*i, so K/V
+        // and the half of load i are compile-time (no clamp)
+        constexpr bool FAST = IPR == 1 && (PT % NW) == 0 && (16 % NW) == 0;
+        if (FAST && pos0 >= range_lo && pos0 + PT - 1 <= range_hi) {
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i) {
-          const int inst = wave + NW * i;  // wave-uniform
-          const int which = inst / (PT * IPR);
-          const int row = (inst / IPR) % PT;
-          const int part = inst % IPR;
-          const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;
-          const int h = rel >> 4;
-          const size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
-                             (size_t)(rel & 15) * POS + part * 1024;
-          __builtin_amdgcn_global_load_lds(
-              (const void*)((which ? a.v : a.k) + off + lane * 16),
-              (__attribute__((address_space(3))) void*)&dst[tile_row(which, row) + part * 1024],
-              16, 0, 0);
+          for (int i = 0; i < (FAST ? DMA_PER_WAVE : 0); ++i) {
+            constexpr int RPW = PT / NW;                 // loads per wave and K (or V)
+            const int which = i / RPW;                   // 0: K, 1: V
+            const int rin = NW * (i % RPW);              // + wave: row within the step
+            dma(which, NH == 1 ? 0 : rin / 16, wave + rin % 16, 0, tile_row(which, wave + rin));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const int inst = wave + NW * i;  // wave-uniform
+            const int which = inst / (PT * IPR);
+            const int row = (inst / IPR) % PT;
+            const int part = inst % IPR;
+            const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
+            dma(which, NH == 1 ? 0 : rel >> 4, rel & 15, part, tile_row(which, row) + part * 1024);
+          }
         }
       } else if (pos0 >= range_lo && pos0 + PT - 1 <= range_hi) {
         // an interior step needs no clamp: row, K/V and page half of chunk u
@@ -354,6 +379,44 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
         // logits z[cb][h][key 16h+4j+i][column r of block cb]; each K operand
         // read from LDS feeds the MFMAs of every column block
         f32x4 z[CB][NH];
+        if constexpr (BF16) {
+          // the step's 2*KCH key operands (half h, chunk c: n = KCH*h + c) in a
+          // software pipeline: the read of operand n + KDEPTH is issued before
+          // the MFMA of operand n, so KDEPTH LDS reads are in flight
+          constexpr int NK = NH * KCH, KDEPTH = 4;
+          f32x4 zz[CB][NH][2];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) zz[cb][h][0] = zz[cb][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          auto kread = [&](int n) {
+            return *reinterpret_cast<const u32x4*>(kt + (n / KCH) * 16 * RSK + (n % KCH) * 64);
+          };
+          u32x4 kring[KDEPTH];
+#pragma unroll
+          for (int n = 0; n < KDEPTH; ++n) kring[n] = kread(n);
+#pragma unroll
+          for (int n = 0; n < NK; ++n) {
+            const u32x4 kop = kring[n % KDEPTH];
+            if (n + KDEPTH < NK) kring[n % KDEPTH] = kread(n + KDEPTH);
+            const int h = n / KCH, c = n % KCH;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+              zz[cb][h][c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, kop), __builtin_bit_cast(bf16x8, qreg[cb][c]),
+                  zz[cb][h][c & 1], 0, 0, 0);
+              if (c == KCH - 1) z[cb][h] = zz[cb][h][0] + zz[cb][h][1];
+            }
+          }
+          // keep the pipeline order through scheduling: the first KDEPTH reads,
+          // then each operand's MFMAs followed by the read KDEPTH ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, KDEPTH, 0);
+#pragma unroll
+          for (int n = 0; n < NK; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
+            if (n + KDEPTH < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           f32x4 z0[CB], z1[CB];
@@ -363,21 +426,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
             z1[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
           const char* kh = kt + h * 16 * RSK;
-          if constexpr (BF16) {
-#pragma unroll
-            for (int c = 0; c < KCH; c += 2) {
-              const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + c * 64));
-              const bf16x8 k1 =
-                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + c * 64 + 64));
-#pragma unroll
-              for (int cb = 0; cb < CB; ++cb) {
-                z0[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    k0, __builtin_bit_cast(bf16x8, qreg[cb][c]), z0[cb], 0, 0, 0);
-                z1[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    k1, __builtin_bit_cast(bf16x8, qreg[cb][c + 1]), z1[cb], 0, 0, 0);
-              }
-            }
-          } else {
+          {
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
               const u32x4 kc = *reinterpret_cast<const u32x4*>(kh + c * 64);
@@ -394,6 +443,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           }
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) z[cb][h] = z0[cb] + z1[cb];
+        }
         }
         // each column keeps the keys of its own mask; online softmax per block
         const int pos0 = step * PT;
@@ -441,11 +491,12 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
             }
             sc.m = m_next;
           }
-          const float m_use = sc.m == -INFINITY ? 0.f : sc.m;
+          // exp(z - m) as 2^(z log2e - m log2e): one fused multiply-add per weight
+          const float m_log = (sc.m == -INFINITY ? 0.f : sc.m) * kLog2e;
 #pragma unroll
           for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[cb][h][i] = exp2_fast((z[cb][h][i] - m_use) * kLog2e);
+            for (int i = 0; i < 4; ++i) p[cb][h][i] = exp2_fast(fmaf(z[cb][h][i], kLog2e, -m_log));
         }
         if constexpr (BF16) {
           // P^T operands: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
