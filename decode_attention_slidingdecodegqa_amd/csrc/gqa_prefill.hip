@@ -53,13 +53,14 @@ constexpr int prefill_waves_per_simd() {
   return BF16 ? 2 : 1;
 }
 
-// waves per work-group and key positions per step.  Global bf16 runs eight
-// waves (128 columns) on one K/V tile: each fetched step feeds twice the MFMA
-// work of a four-wave group, and the 136 KB double buffer allows only one
-// work-group per CU (4.48 ms against 7.09 ms on 2 x 2048 tokens after 8192).
+// waves per work-group and key positions per step.  bf16 runs eight waves
+// (128 columns) on one K/V tile: each fetched step feeds twice the MFMA work
+// of a four-wave group (global: 4.48 ms against 7.09 ms on 2 x 2048 tokens
+// after 8192, where the 138 KB double buffer allows one work-group per CU;
+// sliding: 0.85 ms against 1.08 ms on 8 x 2048 tokens after 4096).
 template <int KV, bool BF16>
 constexpr int prefill_waves() {
-  return (KV == 4 && BF16) ? 8 : 4;
+  return BF16 ? 8 : 4;
 }
 template <int KV, bool BF16>
 constexpr int prefill_step() {
