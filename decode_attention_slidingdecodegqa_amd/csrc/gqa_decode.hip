@@ -111,10 +111,16 @@ struct RopeLds {
 };
 
 // The per-wave LDS tile of the staged (bf16 keys-from-values) path: 16 rows of
-// 512 bf16 values, each row padded by one 16-byte chunk.
+// 512 bf16 values, unpadded, chunk c of row r stored at chunk c ^ f(r) with
+// f(r) = 4(r % 4) + 2((r / 4) % 2).  gfx950 serves a 16-byte-per-lane LDS
+// read in groups of 16 lanes taking rows r = 0..7 of one 16-lane quarter and
+// r = 8..15 of the next: the key-operand reads (row r, chunk 4c + j) then
+// split by parity and the value-operand reads (rows 4j + i, chunk r + 16 blk)
+// by bit 3, so neither has bank conflicts (a 16-byte row pad halves both).
 template <bool KFV, bool BF16>
 constexpr bool kStaged = KFV && BF16;
-constexpr int kStageRow = 512 * 2 + 16;
+constexpr int kStageRow = 512 * 2;
+__device__ __forceinline__ int stage_swz(int r) { return ((r & 3) << 2) | ((r & 4) >> 1); }
 constexpr int kStageTileBytes = kTile * kStageRow;
 // followed by the rebuilt key chunks: 4 slots x 64 lanes x 16 bytes
 constexpr int kStageBytes = kStageTileBytes + 4 * 64 * 16;
@@ -368,7 +374,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     if constexpr (STAGED) {
       if (c < TA) return rot[c * 64 + lane];
       if (c >= TP && c < TP + TA) return rot[(TA + c - TP) * 64 + lane];
-      return *reinterpret_cast<const u32x4*>(stage + r * kStageRow + j * 16 + 64 * c);
+      return *reinterpret_cast<const u32x4*>(stage + r * kStageRow +
+                                             16 * ((4 * c + j) ^ stage_swz(r)));
     } else {
       return kreg[c];
     }
@@ -392,13 +399,13 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     const TileAt nxt = more ? tile_at(it + 1) : cur;
 
     if constexpr (STAGED) {
-      // stage the fetched tile (row r, chunks 4t+j: 16-byte lanes, rows
-      // padded by one chunk so the 16 rows of a lane group hit distinct
-      // banks), rebuild the rotated chunks from the registers, then refill
+      // stage the fetched tile (row r, chunks 4t+j: 16-byte lanes, swizzled
+      // chunks), rebuild the rotated chunks from the registers, then refill
       // the key registers with the next tile at once
-      char* srow = stage + r * kStageRow + j * 16;
+      char* srow = stage + r * kStageRow;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) *reinterpret_cast<u32x4*>(srow + 64 * c) = kreg[c];
+      for (int c = 0; c < KCH; ++c)
+        *reinterpret_cast<u32x4*>(srow + 16 * ((4 * c + j) ^ stage_swz(r))) = kreg[c];
       rebuild_keys(kreg);
       if (more) load_k(nxt);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -445,8 +452,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int blk = 0; blk < VBLK; ++blk)
-          vreg[i][blk] = *reinterpret_cast<const u32x4*>(stage + (4 * j + i) * kStageRow +
-                                                         (r + 16 * blk) * 16);
+          vreg[i][blk] = *reinterpret_cast<const u32x4*>(
+              stage + (4 * j + i) * kStageRow + 16 * ((r ^ stage_swz(4 * j + i)) + 16 * blk));
     } else {
       // the key registers are free: fetch the next tile's keys
       if (more) load_k(nxt);
