@@ -30,10 +30,11 @@ def flags() -> list[str]:
     ]
 
 
-# per-source extra flags: the prefill kernels keep their MFMA accumulators in
-# VGPRs (in AGPRs the compiler copies all of them to VGPRs at every key step,
-# for the rarely taken rescale branch)
+# per-source extra flags: the kernels keep their MFMA accumulators in VGPRs
+# (in AGPRs the compiler copies them to VGPRs and back at every key tile, for
+# the rarely taken online-softmax rescale branch)
 SOURCE_FLAGS = {
+    "gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gqa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
