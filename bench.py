@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run the library's plain read stream and plain copy over BYTES "
                          "bytes (calibrates a profiler's HBM byte counters) and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the prefill workloads (one JSON line) and exit")
     return ap.parse_args()
 
 
@@ -159,6 +161,48 @@ def oracle_sample(sl_case, gl_case, n_sl, n_gl, threads):
     return nbytes, dt
 
 
+def bench_prefill(seed, dev, stream) -> dict:
+    """Times each prefill workload: the call with stream events, the kernel with
+    the library's own HIP events on the launch stream; the algorithmic flops
+    count the unmasked (query, key) pairs."""
+    import torch
+    import decode_attention_slidingdecodegqa_amd as gqa
+    import synth
+
+    log("prefill / chunked prefill (MFMA-bound; algorithmic flops of the unmasked pairs)")
+    pre = {}
+    for name in sorted(synth.PREFILL_WORKLOADS):
+        pc = synth.make_prefill_workload(name, seed=seed, device=dev, fill=0.0)
+        fn = gqa.gqa_prefill_sliding if pc.variant == "sliding" else gqa.gqa_prefill_global
+        o_pf = torch.empty_like(pc.q)
+
+        def pf_call():
+            fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
+               stream=stream)
+
+        for _ in range(2):
+            pf_call()
+        reps = 5
+        gqa.profile_begin(reps + 2)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        for _ in range(reps):
+            pf_call()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        pprof = gqa.profile_read()[(pc.variant, "prefill")]
+        ms = a_ev.elapsed_time(b_ev) / reps
+        fl = pc.flops()
+        pre[name] = {"B": pc.B, "query_rows": pc.N, "seq_len": int(pc.seq_lens[0]),
+                     "cache": "paged16" if pc.block_table is not None else "contiguous",
+                     "us_per_call": round(ms * 1e3, 1),
+                     "kernel_us": round(pprof[1] / max(pprof[0], 1) * 1e3, 1),
+                     "flops_per_call": fl, "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pc, o_pf
+    return pre
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -169,6 +213,17 @@ def main():
 
     if args.copy_probe:
         print(json.dumps(hbm_probes(args.copy_probe)), flush=True)
+        return
+    if args.prefill_only:
+        import torch
+        import decode_attention_slidingdecodegqa_amd as gqa
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        gqa.library()
+        dev = torch.device("cuda:0")
+        print(json.dumps({"prefill": bench_prefill(args.seed, dev, torch.cuda.current_stream(dev))}),
+              flush=True)
         return
 
     import torch
@@ -377,38 +432,7 @@ def main():
         "speedup_vs_stored_keys": round(gl_ms / ms, 3) if ms else None,
         "main_kernel_hbm_traffic": read_traffic("kfv_main"),
     }
-    log("prefill / chunked prefill (MFMA-bound; algorithmic flops of the unmasked pairs)")
-    pre = {}
-    for name in sorted(synth.PREFILL_WORKLOADS):
-        pc = synth.make_prefill_workload(name, seed=args.seed, device=dev, fill=0.0)
-        fn = gqa.gqa_prefill_sliding if pc.variant == "sliding" else gqa.gqa_prefill_global
-        o_pf = torch.empty_like(pc.q)
-
-        def pf_call():
-            fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
-               stream=stream)
-
-        for _ in range(2):
-            pf_call()
-        reps = 5
-        gqa.profile_begin(reps + 2)
-        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_ev.record(stream)
-        for _ in range(reps):
-            pf_call()
-        b_ev.record(stream)
-        torch.cuda.synchronize()
-        pprof = gqa.profile_read()[(pc.variant, "prefill")]
-        ms = a_ev.elapsed_time(b_ev) / reps
-        fl = pc.flops()
-        pre[name] = {"B": pc.B, "query_rows": pc.N, "seq_len": int(pc.seq_lens[0]),
-                     "cache": "paged16" if pc.block_table is not None else "contiguous",
-                     "us_per_call": round(ms * 1e3, 1),
-                     "kernel_us": round(pprof[1] / max(pprof[0], 1) * 1e3, 1),
-                     "flops_per_call": fl, "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
-                     "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        del pc, o_pf
-    line["config"]["prefill"] = pre
+    line["config"]["prefill"] = bench_prefill(args.seed, dev, stream)
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
     line["roofline"]["measured_read_stream_GBps"] = probes["read_GBps"]
