@@ -232,7 +232,12 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       }
     }
   }
-  const u32x4* qrow = myq + (r < G ? r : 0) * NCH;
+  // the wave's query rows in LDS, chunk c of head h at c ^ stage_swz(h) (the
+  // operand reads, lane (r, j) at chunk 4t + j of head r, would otherwise put
+  // eight heads on one bank)
+  const int qh = r < G ? r : 0;
+  const u32x4* qrow = myq + qh * NCH;
+  const int qswz = stage_swz(qh);
 
   // Physical pages of iterations it0 + lane (cur) and it0 + 64 + lane (nxt);
   // block-table entries of pages without an attended position are never read.
@@ -388,7 +393,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
 #pragma unroll
   for (int i = 0; i < QPL; ++i) {
     const int c = lane + 64 * i;
-    if (c < G * NCH) myq[c] = qstage[i];
+    if (c < G * NCH) myq[(c / NCH) * NCH + ((c % NCH) ^ stage_swz(c / NCH))] = qstage[i];
   }
   // one wave writes and reads its own slice: a wavefront-scope fence orders them
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -424,8 +429,9 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
           // columns >= G: zero (stored-key kernels, HBM-bound: a branch around
           // the read costs nothing and the registers are full) or head 0
           // (keys from values, compute-bound)
-          const u32x4 q0 = KFV || r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
-          const u32x4 q1 = KFV || r < G ? qrow[4 * c + 4 + j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 q0 = KFV || r < G ? qrow[(4 * c + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 q1 =
+              KFV || r < G ? qrow[(4 * c + 4 + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
           z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c)),
                                                        __builtin_bit_cast(bf16x8, q0), z0, 0, 0, 0);
           z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c + 1)),
@@ -434,7 +440,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       } else {
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-          const u32x4 qc = KFV || r < G ? qrow[4 * c + j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 qc = KFV || r < G ? qrow[(4 * c + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_f32(kreg[c], e), chunk_f32(qc, e), z0,
