@@ -12,7 +12,8 @@ nodes" table.
 
 Parity status of every function here: pinned by ``tests/test_oracle_pins.py``
 (brute-force masked softmax, torch SDPA in float64, closed forms, bit-exact
-selection, invariants and planted-mistake checks).  The only unpinned reading
+selection, invariants and planted-mistake checks), and for the other entry
+points by ``tests/test_oracle_{append,kfromv,prefill,ring}_pins.py``.  The only unpinned reading
 is the zero row for seq_len <= 0 ("parity unpinned": the pages' shape domain
 starts at S = 1).
 """
@@ -77,6 +78,9 @@ def load(path: str = LIBRARY):
     ap = lib.oracle_gqa_append_rows
     ap.argtypes = [ctypes.c_int, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
     ap.restype = ctypes.c_int
+    rg = lib.oracle_gqa_decode_ring
+    rg.argtypes = [ctypes.c_int, p, p, p, p, i32, i32, i32, i32, i32, p, i32, p, i32]
+    rg.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -141,6 +145,41 @@ def gqa_decode(variant, q, k, v, seq_lens, block_table=None, num_pages=None, row
     rc = lib.oracle_gqa_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(bt), B, cap,
                                max_pages, n_pages, KV, D, W, _ptr(rows_arr), n_rows, _ptr(out),
                                nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
+    return out.reshape(B, HEADS, D) if rows is None else out
+
+
+def gqa_decode_ring(q, k, v, seq_lens, window: int = 1024, rows=None,
+                    nthreads: int | None = None, lib=None) -> np.ndarray:
+    """Reference slidingDecodeGQA over a cache capped at R positions, in fp64.
+
+    k, v [B,R,16,256]: position s in slot s % R (the retrofit page's per-layer
+    caches capped at the window, read as a ring); window <= R; seq_lens may
+    exceed R.  Otherwise as gqa_decode.
+    """
+    KV, D, _ = VARIANTS["sliding"]
+    lib = lib or load()
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share a dtype")
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = q.shape[0]
+    if q.shape != (B, HEADS, D) or seq_lens.shape != (B,):
+        raise ValueError("q must be [B,32,D] and seq_lens [B]")
+    if k.ndim != 4 or k.shape[0] != B or k.shape[2:] != (KV, D) or v.shape != k.shape:
+        raise ValueError("ring k/v must be [B,R,16,256]")
+    ring = k.shape[1]
+    if rows is None:
+        rows_arr, n_rows = None, B * HEADS
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, D), dtype=np.float64)
+    nthreads = nthreads or min(os.cpu_count() or 1, 16)
+    rc = lib.oracle_gqa_decode_ring(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), B, ring, KV,
+                                    D, window, _ptr(rows_arr), n_rows, _ptr(out), nthreads)
     if rc != 0:
         raise ValueError(f"oracle error {rc}: {_ERRORS.get(rc, '?')}")
     return out.reshape(B, HEADS, D) if rows is None else out

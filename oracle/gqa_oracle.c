@@ -28,7 +28,10 @@
  *   - scale is exactly 1 and no logit soft-cap applies to attention;
  *   - L <= 0 yields a zero row (outside the shape domain S >= 1);
  *   - paged pool layout [num_pages, 16, kv, D], logical position s lives in
- *     physical page block_table[b][s/16], slot s%16.
+ *     physical page block_table[b][s/16], slot s%16;
+ *   - a cache capped at R positions (the retrofit page's per-layer caches
+ *     "capped at its window size") is a ring: position s lives in slot s % R
+ *     of [B, R, kv, D], which holds the last R positions written.
  *
  * Arithmetic: every input element is widened exactly to double (bf16 by
  * placing its 16 bits in the top half of an IEEE single), the dot products,
@@ -59,6 +62,7 @@ typedef struct {
   const int32_t *seq_lens;
   const int32_t *block_table; /* NULL: contiguous cache */
   int32_t B, cap, max_pages, num_pages, KV, D, window;
+  int32_t ring;        /* > 0: contiguous ring of `ring` slots, position s in slot s % ring */
   const void *w_k;     /* non-NULL: keys rebuilt from values (global layers) */
   const int32_t *rows; /* (b, h) pairs -- prefill: (token row, h) -- or NULL for every row */
   int32_t n_rows;
@@ -83,6 +87,7 @@ static double orc_elem(const void *base, int dtype, size_t idx) {
 /* Element offset of row (b, position s, kv head g) in k or v; -1 if the
  * block table names a page outside the pool. */
 static int64_t orc_row_offset(const orc_job *j, int b, int64_t s, int g) {
+  if (j->ring > 0) return (((int64_t)b * j->ring + s % j->ring) * j->KV + g) * (int64_t)j->D;
   if (j->block_table == NULL)
     return (((int64_t)b * j->cap + s) * j->KV + g) * (int64_t)j->D;
   int32_t page = j->block_table[(int64_t)b * j->max_pages + s / ORC_PAGE];
@@ -107,7 +112,7 @@ static int orc_one_row(const orc_job *j, int b, int h, double *out) {
   const int g = h / G;             /* kv head of query head h */
   const int64_t L = j->seq_lens[b];
   for (int d = 0; d < D; ++d) out[d] = 0.0;
-  if (L > j->cap) return ORC_ERR_SEQLEN;
+  if (j->ring == 0 && L > j->cap) return ORC_ERR_SEQLEN;
   if (L <= 0) return ORC_OK;
   const int64_t lo = (j->window > 0 && L > j->window) ? L - j->window : 0;
   const int64_t n = L - lo;
@@ -253,14 +258,18 @@ static void *orc_worker(void *arg) {
  */
 static int orc_run(int dtype, const void *q, const void *k, const void *v, const void *w_k,
                    const int32_t *cu_q, int32_t N, const int32_t *seq_lens,
-                   const int32_t *block_table, int32_t B, int32_t cap, int32_t max_pages,
-                   int32_t num_pages, int32_t KV, int32_t D, int32_t window,
-                   const int32_t *rows, int32_t n_rows, double *out, int32_t nthreads) {
+                   const int32_t *block_table, int32_t B, int32_t cap, int32_t ring,
+                   int32_t max_pages, int32_t num_pages, int32_t KV, int32_t D,
+                   int32_t window, const int32_t *rows, int32_t n_rows, double *out,
+                   int32_t nthreads) {
   if (!q || !(k || w_k) || !v || !seq_lens || !out) return ORC_ERR_ARG;
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
   if (B < 1 || cap < 1 || KV < 1 || ORC_HEADS % KV != 0 || D < 1) return ORC_ERR_ARG;
   if (w_k && !(KV == 4 && D == 512)) return ORC_ERR_ARG;
   if (block_table && (max_pages < 1 || num_pages < 1 || cap != max_pages * ORC_PAGE))
+    return ORC_ERR_ARG;
+  /* a ring holds the window: every attended position still has its slot */
+  if (ring < 0 || (ring > 0 && (block_table || cu_q || window < 1 || window > ring)))
     return ORC_ERR_ARG;
   if (cu_q) {
     if (N < 0 || cu_q[0] != 0 || cu_q[B] != N) return ORC_ERR_ARG;
@@ -276,7 +285,7 @@ static int orc_run(int dtype, const void *q, const void *k, const void *v, const
   memset(&j, 0, sizeof j);
   j.dtype = dtype; j.q = q; j.k = k; j.v = v; j.w_k = w_k;
   j.seq_lens = seq_lens; j.block_table = block_table;
-  j.B = B; j.cap = cap; j.max_pages = max_pages; j.num_pages = num_pages;
+  j.B = B; j.cap = cap; j.ring = ring; j.max_pages = max_pages; j.num_pages = num_pages;
   j.KV = KV; j.D = D; j.window = window;
   j.rows = rows; j.n_rows = n_rows; j.out = out;
   j.cu_q = cu_q; j.N = N;
@@ -312,7 +321,7 @@ int oracle_gqa_decode(int dtype, const void *q, const void *k, const void *v,
                       int32_t cap, int32_t max_pages, int32_t num_pages, int32_t KV,
                       int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
                       double *out, int32_t nthreads) {
-  return orc_run(dtype, q, k, v, NULL, NULL, 0, seq_lens, block_table, B, cap, max_pages,
+  return orc_run(dtype, q, k, v, NULL, NULL, 0, seq_lens, block_table, B, cap, 0, max_pages,
                  num_pages, KV, D, window, rows, n_rows, out, nthreads);
 }
 
@@ -331,8 +340,26 @@ int oracle_gqa_decode_k_from_v(int dtype, const void *q, const void *v, const vo
                                const int32_t *rows, int32_t n_rows, double *out,
                                int32_t nthreads) {
   if (!w_k) return ORC_ERR_ARG;
-  return orc_run(dtype, q, NULL, v, w_k, NULL, 0, seq_lens, block_table, B, cap, max_pages,
+  return orc_run(dtype, q, NULL, v, w_k, NULL, 0, seq_lens, block_table, B, cap, 0, max_pages,
                  num_pages, 4, 512, 0, rows, n_rows, out, nthreads);
+}
+
+/*
+ * oracle_gqa_decode_ring -- slidingDecodeGQA over a cache capped at `ring`
+ * positions.  The retrofit page ("Progressive Window Assignment") gives each
+ * sliding layer its own KV cache capped at its window size; read as a ring,
+ * position s lives in slot s % ring of k, v [B, ring, KV, D], so the slots
+ * hold the last `ring` positions and the window [max(0, L-W), L) needs
+ * window <= ring.  Otherwise as oracle_gqa_decode (contiguous; seq_lens may
+ * exceed ring).
+ */
+int oracle_gqa_decode_ring(int dtype, const void *q, const void *k, const void *v,
+                           const int32_t *seq_lens, int32_t B, int32_t ring, int32_t KV,
+                           int32_t D, int32_t window, const int32_t *rows, int32_t n_rows,
+                           double *out, int32_t nthreads) {
+  if (ring < 1) return ORC_ERR_ARG;
+  return orc_run(dtype, q, k, v, NULL, NULL, 0, seq_lens, NULL, B, ring, ring, 0, 0, KV, D,
+                 window, rows, n_rows, out, nthreads);
 }
 
 /*
@@ -356,7 +383,7 @@ int oracle_gqa_prefill(int dtype, const void *q, const void *k, const void *v,
                        int32_t window, const int32_t *rows, int32_t n_rows, double *out,
                        int32_t nthreads) {
   if (!cu_q || !k) return ORC_ERR_ARG;
-  return orc_run(dtype, q, k, v, NULL, cu_q, N, seq_lens, block_table, B, cap, max_pages,
+  return orc_run(dtype, q, k, v, NULL, cu_q, N, seq_lens, block_table, B, cap, 0, max_pages,
                  num_pages, KV, D, window, rows, n_rows, out, nthreads);
 }
 

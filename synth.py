@@ -224,6 +224,38 @@ def make_case(variant: str, dtype: str, B: int, cap: int, seq_lens, paged: bool 
                 w_k.to(tdt))
 
 
+def make_ring_case(dtype: str, B: int, ring: int, seq_lens, seed: int = 0, device="cpu",
+                   fill: float = float("nan"), window: int = 1024) -> Case:
+    """A sliding-layer cache capped at ``ring`` positions: k, v [B, ring, 16, 256]
+    with position s in slot s % ring, holding the last min(L, ring) positions
+    of each sequence.  The rows are the ones ``make_case(..., draw_from=L -
+    ring)`` draws for the same positions (same seed and order); unused slots
+    hold ``fill``.  seq_lens may exceed ring."""
+    KV, D, _ = VARIANTS["sliding"]
+    tdt = TORCH_DTYPES[dtype]
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int32).cpu()
+    assert seq_lens.shape == (B,)
+    g_w = _gen(seed, 2, device)
+    w_q = torch.empty(D, device=device).uniform_(0.2, 0.4, generator=g_w)
+    w_k = torch.empty(D, device=device).uniform_(0.2, 0.4, generator=g_w)
+    g_q = _gen(seed, 3, device)
+    q = (w_q * rms_unit(torch.randn(B, HEADS, D, generator=g_q, device=device))).to(tdt)
+    k = torch.full((B, ring, KV, D), fill, dtype=tdt, device=device)
+    v = torch.full((B, ring, KV, D), fill, dtype=tdt, device=device)
+    for b in range(B):
+        L = int(seq_lens[b])
+        n = max(0, min(L, ring))
+        if n == 0:
+            continue
+        g = _gen(seed, 1000 + b, device)
+        kx = rms_unit(torch.randn(n, KV, D, generator=g, device=device))
+        vx = rms_unit(torch.randn(n, KV, D, generator=g, device=device))
+        slots = torch.arange(L - n, L, device=device) % ring
+        k[b, slots] = (w_k * kx).to(tdt)
+        v[b, slots] = vx.to(tdt)
+    return Case("sliding", dtype, q, k, v, seq_lens.to(device), None, ring, window, w_k.to(tdt))
+
+
 @dataclasses.dataclass
 class PrefillCase:
     """A chunk of T_b new tokens per sequence, already appended to the cache:
