@@ -432,6 +432,36 @@ def main():
         "speedup_vs_stored_keys": round(gl_ms / ms, 3) if ms else None,
         "main_kernel_hbm_traffic": read_traffic("kfv_main"),
     }
+    log("slidingDecodeGQA over caches capped at the window (ring of 1024 slots), "
+        "B=256, seq_lens U[1,262144]")
+    ring_lens = synth.draw_seq_lens(("uniform", 1, 262144), 256, args.seed)
+    rg = synth.make_ring_case("bf16", 256, 1024, ring_lens, seed=args.seed, device=dev,
+                              fill=0.0, window=1024)
+    o_rg = torch.empty_like(rg.q)
+    ws_rg_n = gqa.gqa_decode_sliding_ring_workspace_bytes(256, 1024, 1024)
+    ws_rg = torch.empty(max(ws_rg_n, 256), dtype=torch.uint8, device=dev)
+
+    def ring_call():
+        gqa.gqa_decode_sliding_ring(rg.q, rg.k, rg.v, rg.seq_lens, window=1024, o=o_rg,
+                                    workspace=ws_rg, stream=stream)
+
+    for _ in range(2):
+        ring_call()
+    reps = max(3, min(args.steps, 10))
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record(stream)
+    for _ in range(reps):
+        ring_call()
+    b_ev.record(stream)
+    torch.cuda.synchronize()
+    ms = a_ev.elapsed_time(b_ev) / reps
+    rg_bytes = int(torch.clamp(ring_lens.to(torch.int64), max=1024).sum()) * 16 * 256 * 2 * 2
+    line["config"]["sliding_ring"] = {
+        "B": 256, "ring_slots": 1024, "window": 1024, "seq_lens": "U[1,262144]",
+        "cache_bytes": 2 * rg.k.numel() * 2, "kv_bytes_per_call": rg_bytes,
+        "us_per_call": round(ms * 1e3, 2), "kv_GBps": round(rg_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(rg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del rg, o_rg, ws_rg
     line["config"]["prefill"] = bench_prefill(args.seed, dev, stream)
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)

@@ -12,6 +12,9 @@ the library is missing or no GPU is present the calls raise.
     gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens)
     gqa_decode_sliding_window(q, k, v, seq_lens, window)    sliding geometry, runtime window
     gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, window)
+    gqa_decode_sliding_ring(q, k, v, seq_lens, window)  sliding cache capped at R positions
+                                                        (k, v [B,R,16,256], slot s % R)
+    gqa_append_sliding_ring(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache)
     gqa_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
     gqa_append_global(q_raw, k_raw, w_q, w_k, seq_lens, k_cache, v_cache[, block_table])
                                                         new token: norms, RoPE, cache write
@@ -41,6 +44,7 @@ from ._lib import (  # noqa: F401
     gqa_append_global,
     gqa_append_global_k_eq_v,
     gqa_append_sliding,
+    gqa_append_sliding_ring,
     gqa_decode_global,
     gqa_decode_global_k_eq_v,
     gqa_decode_global_k_eq_v_paged,
@@ -49,6 +53,8 @@ from ._lib import (  # noqa: F401
     gqa_decode_sliding,
     gqa_decode_sliding_paged,
     gqa_decode_sliding_window,
+    gqa_decode_sliding_ring,
+    gqa_decode_sliding_ring_workspace_bytes,
     gqa_decode_sliding_window_paged,
     gqa_decode_workspace_bytes,
     gqa_prefill_global,

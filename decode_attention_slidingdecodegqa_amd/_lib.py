@@ -24,7 +24,8 @@ EXPORTED_SYMBOLS = (
     "gqa_append_global", "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
     "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
     "gqa_append_global_k_eq_v_paged", "gqa_prefill_sliding", "gqa_prefill_global",
-    "gqa_prefill_sliding_paged", "gqa_prefill_global_paged",
+    "gqa_prefill_sliding_paged", "gqa_prefill_global_paged", "gqa_decode_sliding_ring",
+    "gqa_decode_sliding_ring_workspace_bytes", "gqa_append_sliding_ring",
 )
 
 
@@ -62,6 +63,12 @@ def library():
     lib.gqa_decode_sliding_window_workspace_bytes.restype = sz
     lib.gqa_decode_sliding_window_plan.argtypes = [i32, i32, i32] + [ctypes.POINTER(i32)] * 3
     lib.gqa_decode_sliding_window_plan.restype = ctypes.c_int
+    lib.gqa_decode_sliding_ring.argtypes = [p, p, p, p, p, i32, i32, i32, i32, p, sz, p]
+    lib.gqa_decode_sliding_ring.restype = ctypes.c_int
+    lib.gqa_decode_sliding_ring_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.gqa_decode_sliding_ring_workspace_bytes.restype = sz
+    lib.gqa_append_sliding_ring.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, p]
+    lib.gqa_append_sliding_ring.restype = ctypes.c_int
     lib.gqa_append_sliding.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, p]
     lib.gqa_append_sliding_paged.argtypes = [p, p, p, p, p, p, i32, p, p, p, p, i32, i32, i32, p]
     lib.gqa_append_global.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, p]
@@ -318,7 +325,7 @@ def gqa_decode_sliding_window_paged(q, k_pool, v_pool, block_table, seq_lens, wi
 
 
 def _append_call(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
-                 block_table, q_out, stream):
+                 block_table, q_out, stream, ring=False):
     KV = 16 if variant == GQA_SLIDING else 4
     D = 256 if variant == GQA_SLIDING else 512
     B = q_raw.shape[0]
@@ -346,6 +353,8 @@ def _append_call(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_ca
     ptrs += [_dev(w_q, "w_q"), _dev(w_k, "w_k")]
     dt = _dtype_code(q_raw)
     name = "gqa_append_" + ("sliding" if variant == GQA_SLIDING else "global")
+    if ring:
+        name += "_ring"
     if block_table is None:
         if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[2:] != (KV, D) or \
                 v_cache.shape != k_cache.shape:
@@ -368,6 +377,44 @@ def _append_call(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_ca
     if rc:
         raise GqaError(name, rc)
     return q_out
+
+
+def gqa_decode_sliding_ring_workspace_bytes(B: int, ring: int, window: int = 1024) -> int:
+    """Workspace bytes of gqa_decode_sliding_ring (0: none needed, or bad arguments)."""
+    return int(library().gqa_decode_sliding_ring_workspace_bytes(int(B), int(ring), int(window)))
+
+
+def gqa_decode_sliding_ring(q, k, v, seq_lens, window: int = 1024, o=None, workspace=None,
+                            stream=None):
+    """slidingDecodeGQA over a cache capped at R positions: k, v [B,R,16,256] with
+    position s in slot s % R (R a multiple of 16, window <= R); seq_lens may
+    exceed R."""
+    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != (16, 256) or \
+            v.shape != k.shape:
+        raise ValueError("k/v must be [B,R,16,256]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    ring = k.shape[1]
+    B = q.shape[0]
+    need = gqa_decode_sliding_ring_workspace_bytes(B, ring, window)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    B, o, ws, ws_bytes = _prepare(GQA_SLIDING, q, seq_lens, o, workspace, ring, window)
+    rc = library().gqa_decode_sliding_ring(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                           _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, ring,
+                                           int(window), _dtype_code(q), ws, ws_bytes,
+                                           _stream(stream, q.device))
+    if rc:
+        raise GqaError("gqa_decode_sliding_ring", rc)
+    return o
+
+
+def gqa_append_sliding_ring(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
+                            q_out=None, stream=None):
+    """The sliding append into a cache capped at R positions (k_cache, v_cache
+    [B,R,16,256]): the new token's rows go to slot (seq_lens-1) % R."""
+    return _append_call(GQA_SLIDING, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,
+                        None, q_out, stream, ring=True)
 
 
 def gqa_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_cache,

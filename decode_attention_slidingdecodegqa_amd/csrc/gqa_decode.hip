@@ -59,7 +59,12 @@ struct KernelArgs {
   int32_t num_pages;
   int32_t window;
   int32_t n_waves;
+  int32_t ring;  // > 0: contiguous cache capped at `ring` positions, position s in slot s % ring
 };
+
+// Capacity that bounds a sequence's positions: the cache's, or for a ring
+// (whose slots hold the last `ring` positions) the position domain.
+__device__ inline int position_cap(int cap, int ring) { return ring > 0 ? kMaxSeq : cap; }
 
 // Attended range of one sequence: positions [lo, L), tiles [t0, t0 + n).
 struct SeqRange {
@@ -271,7 +276,9 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       off = ((size_t)(ta.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
     } else {
       ta.ok = true;
-      off = (((size_t)b * a.cap + ta.pos0) * KV + g) * (size_t)ROW;
+      // a ring of a multiple of 16 slots never splits a 16-aligned tile
+      const int slot0 = a.ring > 0 ? ta.pos0 % a.ring : ta.pos0;
+      off = (((size_t)b * a.cap + slot0) * KV + g) * (size_t)ROW;
     }
     ta.kb = (KFV ? a.v : a.k) + off;
     ta.vb = a.v + off;
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
     for (int i = 0; i < 4; ++i) {
       const int b = 4 * lane + i;
       const int L = b < a.B ? a.seq_lens[b] : 0;
-      cnt[i] = seq_range(L, a.cap, a.window).n;
+      cnt[i] = seq_range(L, position_cap(a.cap, a.ring), a.window).n;
       if (b < a.B) {
         s_len[b] = L;
         s_cnt[b] = cnt[i];
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   long t = s_begin;
   while (t < s_end) {
     // ---- one segment: tiles [k_begin, k_end) of unit (b, g)
-    const SeqRange sr = seq_range(s_len[b], a.cap, a.window);
+    const SeqRange sr = seq_range(s_len[b], position_cap(a.cap, a.ring), a.window);
     const int k_begin = kk0;
     const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
     accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin, k_end, 1,
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   const int unit = blockIdx.x;
   const int b = unit / KV;
   const int g = unit % KV;
-  const SeqRange sr = seq_range(a.seq_lens[b], a.cap, a.window);
+  const SeqRange sr = seq_range(a.seq_lens[b], position_cap(a.cap, a.ring), a.window);
   if (sr.n == 0) {  // nothing attended: zero rows
     for (int c = threadIdx.x; c < G * NCH; c += kThreads)
       *reinterpret_cast<u32x4*>(a.o + ((size_t)b * kHeads + g * G + c / NCH) * ROW + (c % NCH) * 16) =
@@ -889,6 +896,7 @@ struct AppendArgs {
   int32_t cap;
   int32_t max_pages;
   int32_t num_pages;
+  int32_t ring;  // > 0: contiguous cache capped at `ring` positions (slot s % ring)
 };
 
 template <int N, bool BF16>
@@ -946,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int L = a.seq_lens[b];
-  const bool live = L >= 1 && L <= a.cap;
+  const bool live = L >= 1 && L <= position_cap(a.cap, a.ring);
   const int row = blockIdx.y * kWaves + wave;
   const int pos = L - 1;
 
@@ -959,7 +967,7 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
       write_cache = page >= 0 && page < a.num_pages;
       row_off = ((size_t)(write_cache ? page : 0) * kPage + pos % kPage) * KV * (size_t)ROW;
     } else {
-      row_off = ((size_t)b * a.cap + pos) * KV * (size_t)ROW;
+      row_off = ((size_t)b * a.cap + (a.ring > 0 ? pos % a.ring : pos)) * KV * (size_t)ROW;
     }
   }
 
@@ -1167,10 +1175,12 @@ constexpr int kProfKeysFromValues = 6;
 
 // w_k != nullptr: global layers over a values-only cache (k unused, keys
 // rebuilt from v)
+// ring > 0: sliding layers over a contiguous cache capped at `ring` positions
+// (S_max = ring; 16 <= ring <= 262144, a multiple of 16, window <= ring)
 int run(int variant, int window, bool paged, const void* q, const void* k, const void* v,
         const void* w_k, const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
         void* o, int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype, void* workspace,
-        size_t workspace_bytes_given, void* stream_) {
+        size_t workspace_bytes_given, void* stream_, int32_t ring = 0) {
   const bool kfv = w_k != nullptr;
   if (kfv && variant != GQA_GLOBAL) return GQA_ERR_DTYPE;
   if (!q || (!k && !kfv) || !v || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
@@ -1184,12 +1194,17 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
     if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
     cap = S_max;
   }
+  if (ring != 0) {
+    if (variant != GQA_SLIDING || kfv || paged) return GQA_ERR_DTYPE;
+    if (ring < kTile || ring > kMaxSeq || ring % kTile != 0 || ring != S_max) return GQA_ERR_SHAPE;
+    if (window < 1 || window > ring) return GQA_ERR_SHAPE;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(w_k))
     return GQA_ERR_ALIGN;
   VariantInfo vi;
   variant_info(variant, &vi);
   Plan plan;
-  int rc = make_plan(variant, B, cap, window, &plan);
+  int rc = make_plan(variant, B, ring ? kMaxSeq : cap, window, &plan);
   if (rc) return rc;
   const bool unit_mode = plan.mode == GQA_MODE_UNIT;
   if (!unit_mode) {
@@ -1217,6 +1232,7 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ka.num_pages = paged ? num_pages : 0;
   ka.window = window;
   ka.n_waves = plan.waves;
+  ka.ring = ring;
 
   MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(unit_mode, paged, bf16)
                    : kfv                   ? pick_main<4, 512, true>(unit_mode, paged, bf16)
@@ -1256,11 +1272,12 @@ AppendFn pick_append(bool paged, bool bf16) {
 
 // k_cache == nullptr with values_only: global layers over a values-only cache
 // (the key row is not written; attention rebuilds it from the value row)
+// ring > 0: sliding layers over a contiguous cache capped at `ring` positions
 int run_append(int variant, bool paged, bool values_only, const void* q_raw, const void* k_raw,
                const void* v_raw, const void* w_q, const void* w_k, const int32_t* block_table,
                int32_t max_pages, const int32_t* seq_lens, void* q_out, void* k_cache,
                void* v_cache, int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype,
-               void* stream_) {
+               void* stream_, int32_t ring = 0) {
   const bool global = variant == GQA_GLOBAL;
   if (values_only && !global) return GQA_ERR_DTYPE;
   if (!q_raw || !k_raw || (!global && !v_raw) || !w_q || !w_k || !seq_lens || !q_out ||
@@ -1275,6 +1292,10 @@ int run_append(int variant, bool paged, bool values_only, const void* q_raw, con
   } else {
     if (S_max < 1 || S_max > kMaxSeq) return GQA_ERR_SHAPE;
     cap = S_max;
+  }
+  if (ring != 0) {
+    if (global || paged) return GQA_ERR_DTYPE;
+    if (ring < kTile || ring > kMaxSeq || ring % kTile != 0 || ring != S_max) return GQA_ERR_SHAPE;
   }
   if (!aligned16(q_raw) || !aligned16(k_raw) || (!global && !aligned16(v_raw)) ||
       !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_out) || !aligned16(k_cache) ||
@@ -1295,6 +1316,7 @@ int run_append(int variant, bool paged, bool values_only, const void* q_raw, con
   aa.cap = cap;
   aa.max_pages = paged ? max_pages : 0;
   aa.num_pages = paged ? num_pages : 0;
+  aa.ring = ring;
   const bool bf16 = dtype == GQA_BF16;
   AppendFn fn = global ? pick_append<4, 512>(paged, bf16) : pick_append<16, 256>(paged, bf16);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
@@ -1392,6 +1414,30 @@ int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, 
   if (n_waves) *n_waves = p.waves;
   if (n_slots) *n_slots = p.slots;
   return GQA_OK;
+}
+
+int gqa_decode_sliding_ring(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                            void* o, int32_t B, int32_t ring, int32_t window, int32_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 1) return GQA_ERR_SHAPE;
+  return run(GQA_SLIDING, window, false, q, k, v, nullptr, nullptr, 0, seq_lens, o, B, ring, 0,
+             dtype, workspace, workspace_bytes, stream, ring);
+}
+
+size_t gqa_decode_sliding_ring_workspace_bytes(int32_t B, int32_t ring, int32_t window) {
+  Plan p;
+  if (window < 1 || ring < kTile || ring > kMaxSeq || ring % kTile != 0 || window > ring ||
+      make_plan(GQA_SLIDING, B, kMaxSeq, window, &p))
+    return 0;
+  return p.total;
+}
+
+int gqa_append_sliding_ring(const void* q_raw, const void* k_raw, const void* v_raw,
+                            const void* w_q, const void* w_k, const int32_t* seq_lens,
+                            void* q_out, void* k_cache, void* v_cache, int32_t B, int32_t ring,
+                            int32_t dtype, void* stream) {
+  return run_append(GQA_SLIDING, false, false, q_raw, k_raw, v_raw, w_q, w_k, nullptr, 0,
+                    seq_lens, q_out, k_cache, v_cache, B, ring, 0, dtype, stream, ring);
 }
 
 int gqa_append_sliding(const void* q_raw, const void* k_raw, const void* v_raw, const void* w_q,

@@ -130,6 +130,22 @@ size_t gqa_decode_sliding_window_workspace_bytes(int32_t B, int32_t capacity, in
 int gqa_decode_sliding_window_plan(int32_t B, int32_t capacity, int32_t window, int32_t* mode,
                                    int32_t* n_waves, int32_t* n_slots);
 
+/* slidingDecodeGQA over a cache capped at `ring` positions.  The Retrofit Plan
+ * page ("Progressive Window Assignment") gives each sliding layer its own KV
+ * cache capped at its window size; read as a ring, k and v are
+ * [B, ring, 16, 256] with position s in slot s % ring, so the slots hold the
+ * last `ring` positions written (gqa_append_sliding_ring writes them).
+ * seq_lens[b] may exceed ring (up to 262144); the call attends to
+ * [max(0, L-window), L) as gqa_decode_sliding_window does.  Requires
+ * 16 <= ring <= 262144, ring a multiple of 16 (a 16-position tile then never
+ * wraps) and 1 <= window <= ring (GQA_ERR_SHAPE otherwise).  Other arguments,
+ * ownership and errors as for gqa_decode_sliding; the workspace size comes from
+ * gqa_decode_sliding_ring_workspace_bytes (0: none needed, or bad arguments). */
+int gqa_decode_sliding_ring(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                            void* o, int32_t B, int32_t ring, int32_t window, int32_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+size_t gqa_decode_sliding_ring_workspace_bytes(int32_t B, int32_t ring, int32_t window);
+
 /* KV append of the new token with its per-head norms and RoPE: the nodes
  * attn.qk_norm, attn.v_norm and attn.rope of the Model Spec page's
  * "Compute-graph nodes" table, applied to one new token per sequence at
@@ -159,6 +175,15 @@ int gqa_append_sliding_paged(const void* q_raw, const void* k_raw, const void* v
                              int32_t max_pages, const int32_t* seq_lens, void* q_out,
                              void* k_pool, void* v_pool, int32_t B, int32_t num_pages,
                              int32_t dtype, void* stream);
+/* The sliding append into a cache capped at `ring` positions (layout and
+ * requirements as gqa_decode_sliding_ring): the new token's rows go to slot
+ * (seq_lens[b] - 1) % ring, the rotation uses the true position
+ * seq_lens[b] - 1; seq_lens[b] outside [1, 262144] gets zero q_out rows and no
+ * cache write. */
+int gqa_append_sliding_ring(const void* q_raw, const void* k_raw, const void* v_raw,
+                            const void* w_q, const void* w_k, const int32_t* seq_lens,
+                            void* q_out, void* k_cache, void* v_cache, int32_t B, int32_t ring,
+                            int32_t dtype, void* stream);
 int gqa_append_global(const void* q_raw, const void* k_raw, const void* w_q, const void* w_k,
                       const int32_t* seq_lens, void* q_out, void* k_cache, void* v_cache,
                       int32_t B, int32_t S_max, int32_t dtype, void* stream);

@@ -151,6 +151,31 @@ def test_window_arguments(lib):
         gqa.gqa_decode_plan("global", 4, 4096, window=1024)
 
 
+def test_ring_arguments_fail_before_launch(lib):
+    P = ctypes.c_void_p
+    ok, mis = P(0x10000), P(0x10008)
+    f, ap = lib.gqa_decode_sliding_ring, lib.gqa_append_sliding_ring
+    for ring, window in ((1000, 1000), (8, 8), (262160, 1024), (1024, 1025), (1024, 0),
+                         (0, 1024), (-16, 8)):
+        assert f(ok, ok, ok, ok, ok, 4, ring, window, 1, None, 0, None) == -2, (ring, window)
+        assert lib.gqa_decode_sliding_ring_workspace_bytes(4, ring, window) == 0
+    assert f(ok, ok, ok, ok, ok, 4, 1024, 1024, 7, None, 0, None) == -3
+    assert f(ok, ok, ok, None, ok, 4, 1024, 1024, 1, None, 0, None) == -1
+    assert f(ok, mis, ok, ok, ok, 4, 1024, 1024, 1, None, 0, None) == -4
+    # a small batch runs in stream mode: its workspace is required
+    assert gqa.gqa_decode_sliding_ring_workspace_bytes(4, 1024, 1024) > 0
+    assert f(ok, ok, ok, ok, ok, 4, 1024, 1024, 1, None, 0, None) == -5
+    # the ring plans over the position domain, as a full-length windowed call
+    for B, ring, w in ((4, 1024, 1024), (256, 1024, 1024), (256, 8192, 8192), (7, 48, 17)):
+        assert gqa.gqa_decode_sliding_ring_workspace_bytes(B, ring, w) == \
+            gqa.gqa_decode_workspace_bytes("sliding", B, 262144, window=w)
+    for ring in (1000, 8, 0):
+        assert ap(ok, ok, ok, ok, ok, ok, ok, ok, ok, 4, ring, 1, None) == -2
+    assert ap(ok, ok, None, ok, ok, ok, ok, ok, ok, 4, 1024, 1, None) == -1
+    assert ap(ok, ok, ok, ok, ok, ok, ok, ok, ok, 4, 1024, 7, None) == -3
+    assert ap(ok, ok, ok, ok, ok, ok, ok, mis, ok, 4, 1024, 1, None) == -4
+
+
 def test_append_arguments_fail_before_launch(lib):
     P = ctypes.c_void_p
     ok, mis = P(0x10000), P(0x10008)
