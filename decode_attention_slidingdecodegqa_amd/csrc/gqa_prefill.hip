@@ -38,9 +38,11 @@ struct PrefillArgs {
 constexpr int kXcds = 8;
 
 // 16-column MFMA blocks per wave.  Two blocks would let every K/V operand read
-// from LDS feed two MFMAs, but they need one wave per SIMD; measured on the
-// sliding kernel, two waves per SIMD with one block each hide more latency
-// (1172 us against 1501 us on 8 x 2048 tokens), so every variant runs one.
+// from LDS feed two MFMAs, but their queries and accumulators do not fit the
+// 256 registers of two waves per SIMD (D = 256: 548 bytes per lane of spills;
+// D = 512 needs the whole register file), and one wave per SIMD hides less
+// latency (sliding: 1501 us against 1172 us when measured), so every variant
+// runs one.
 template <int KV, bool BF16>
 constexpr int prefill_col_blocks() {
   return 1;
