@@ -795,75 +795,132 @@ struct CombineArgs {
   int32_t n_waves;
 };
 
-// One work-group per (sequence, query head); thread t owns d = 4t .. 4t+3.
-// Merges the partials of a unit that several waves' slices share; a unit held
-// by one slice was written by its wave, and a sequence with nothing attended
-// gets a zero row.
+// One work-group of kCombineWaves waves per (sequence, query head).  Wave w
+// merges the partials w, w + kCombineWaves, ... of the unit (lane l owns
+// d = (D/64) l .. (D/64)(l+1) - 1, U partials in flight), then the waves'
+// sums are added in LDS in wave order.  A unit held by one slice was written
+// by its wave; a sequence with nothing attended gets a zero row.  With few
+// sequences a unit spans hundreds of slices, so the waves' loads in flight
+// set the combine's time.
+constexpr int kCombineWaves = 8;
+
 template <int KV, int D, bool BF16>
-__global__ __launch_bounds__(D / 4) void gqa_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(CombineArgs a) {
   constexpr int G = kHeads / KV;
   constexpr int EB = Elem<BF16>::bytes;
-  constexpr int U = 8;  // partials in flight per thread
+  constexpr int PER = D / 64;  // d values per lane
+  constexpr int NV = PER / 4;  // 16-byte chunks per lane
+  constexpr int U = 8;         // partials in flight per lane
+  __shared__ __attribute__((aligned(16))) float s_acc[kCombineWaves][D];
+  __shared__ float s_l[kCombineWaves];
   const int b = blockIdx.x / kHeads;
   const int h = blockIdx.x % kHeads;
   const int g = h / G;
   const int hh = h % G;
   const int unit = b * KV + g;
-  const int d = threadIdx.x * 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int d = lane * PER;
   char* dst = a.o + ((size_t)b * kHeads + h) * D * EB + (size_t)d * EB;
+
+  auto store = [&](const float (&run)[PER]) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      if constexpr (BF16) {
+        *reinterpret_cast<u32x2*>(dst + 4 * c * EB) =
+            u32x2{bf16_pack2(run[4 * c], run[4 * c + 1]), bf16_pack2(run[4 * c + 2], run[4 * c + 3])};
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 4 * c * EB) =
+            f32x4{run[4 * c], run[4 * c + 1], run[4 * c + 2], run[4 * c + 3]};
+      }
+    }
+  };
 
   const int P0 = a.prefix[b];
   const int n = (a.prefix[b + 1] - P0) / KV;
-  float run[4] = {0.f, 0.f, 0.f, 0.f};
-  if (n > 0) {
-    const long T = a.prefix[a.B];
-    const long s0 = P0 + (long)g * n;
-    const int wf = wave_of(s0, T, a.n_waves);
-    const int wl = wave_of(s0 + n - 1, T, a.n_waves);
-    if (wf == wl) return;  // written by the wave that held the whole unit
-    const int ns = wl - wf + 1;
-    const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + ((size_t)unit + wf) * G + hh;
-    const float* accp = a.ws_acc + (((size_t)unit + wf) * G + hh) * D + d;
-    const size_t sstride = (size_t)G * D;
-    // waves between wf and wl whose slices are empty (more waves than tiles)
-    // wrote nothing: their slots are skipped
-    auto holds = [&](int s) {
-      const long w = wf + s;
-      return (w + 1) * T / a.n_waves > w * T / a.n_waves;
-    };
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) {
-      if (!holds(s)) continue;
-      const f32x2 x = ml[(size_t)s * G];
-      if (x[1] > 0.f) M = fmaxf(M, x[0]);
-    }
-    f32x4 A = {0.f, 0.f, 0.f, 0.f};
-    float Lt = 0.f;
-    for (int s0u = 0; s0u < ns; s0u += U) {
-      f32x4 x[U];
-      float wgt[U];
+  if (n <= 0) {
+    if (wave == 0) {
+      float zero[PER];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0u + u < ns ? s0u + u : ns - 1;
-        const f32x2 e = ml[(size_t)s * G];
-        const bool ok = s0u + u < ns && holds(s) && e[1] > 0.f;
-        wgt[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
-        Lt += wgt[u] * (ok ? e[1] : 0.f);
-        x[u] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride);
-        x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < PER; ++e) zero[e] = 0.f;
+      store(zero);
+    }
+    return;
+  }
+  const long T = a.prefix[a.B];
+  const long s0 = P0 + (long)g * n;
+  const int wf = wave_of(s0, T, a.n_waves);
+  const int wl = wave_of(s0 + n - 1, T, a.n_waves);
+  if (wf == wl) return;  // written by the wave that held the whole unit
+  const int ns = wl - wf + 1;
+  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + ((size_t)unit + wf) * G + hh;
+  const float* accp = a.ws_acc + (((size_t)unit + wf) * G + hh) * D + d;
+  const size_t sstride = (size_t)G * D;
+  // waves between wf and wl whose slices are empty (more waves than tiles)
+  // wrote nothing: their slots are skipped
+  auto holds = [&](int s) {
+    const long w = wf + s;
+    return (w + 1) * T / a.n_waves > w * T / a.n_waves;
+  };
+  // the reference max over the partials, lane-parallel in every wave
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) {
+    if (!holds(s)) continue;
+    const f32x2 x = ml[(size_t)s * G];
+    if (x[1] > 0.f) M = fmaxf(M, x[0]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  f32x4 A[NV];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) A[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float Lt = 0.f;
+  for (int s0u = wave; s0u < ns; s0u += kCombineWaves * U) {
+    f32x4 x[U][NV];
+    float wgt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = s0u + kCombineWaves * u;
+      const int s = su < ns ? su : ns - 1;
+      const f32x2 e = ml[(size_t)s * G];
+      const bool ok = su < ns && holds(s) && e[1] > 0.f;
+      wgt[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
+      Lt += wgt[u] * (ok ? e[1] : 0.f);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        x[u][c] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride + 4 * c);
+        x[u][c] = ok ? x[u][c] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) A += wgt[u] * x[u];
     }
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    for (int c = 0; c < 4; ++c) run[c] = Lt > 0.f ? A[c] * inv : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < NV; ++c) A[c] += wgt[u] * x[u][c];
   }
-  if constexpr (BF16) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{bf16_pack2(run[0], run[1]),
-                                           bf16_pack2(run[2], run[3])};
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{run[0], run[1], run[2], run[3]};
+#pragma unroll
+  for (int c = 0; c < NV; ++c) *reinterpret_cast<f32x4*>(&s_acc[wave][d + 4 * c]) = A[c];
+  if (lane == 0) s_l[wave] = Lt;
+  __syncthreads();
+  if (wave != 0) return;
+  float L = 0.f;
+  float run[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) run[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    L += s_l[w];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&s_acc[w][d + 4 * c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) run[4 * c + e] += v[e];
+    }
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) run[e] = L > 0.f ? run[e] * inv : 0.f;
+  store(run);
 }
 
 // ------------------------------------------------------------- KV append
@@ -1255,7 +1312,7 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
       variant == GQA_SLIDING ? pick_combine<16, 256>(bf16) : pick_combine<4, 512>(bf16);
   ProfRec* pc = prof_slot(kfv ? kProfKeysFromValues + 1 : 2 * variant + 1);
   if (pc) hipEventRecord(pc->start, stream);
-  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3((unsigned)(vi.D / 4)), 0, stream, ca);
+  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3(64u * kCombineWaves), 0, stream, ca);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (pc) hipEventRecord(pc->stop, stream);
   return GQA_OK;
