@@ -462,6 +462,34 @@ def main():
         "us_per_call": round(ms * 1e3, 2), "kv_GBps": round(rg_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(rg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del rg, o_rg, ws_rg
+    log("one sequence of 262144 positions (paged), both geometries")
+    b1 = {}
+    for name in ("global_bf16_b1_paged_s262144", "sliding_bf16_b1_paged_s262144"):
+        c1 = synth.make_workload(name, seed=args.seed, device=dev, fill=0.0)
+        fn1 = gqa.gqa_decode_global_paged if c1.variant == "global" else gqa.gqa_decode_sliding_paged
+        o1 = torch.empty_like(c1.q)
+        ws1 = torch.empty(max(gqa.gqa_decode_workspace_bytes(c1.variant, c1.B, c1.cap), 256),
+                          dtype=torch.uint8, device=dev)
+
+        def b1_call():
+            fn1(c1.q, c1.k, c1.v, c1.block_table, c1.seq_lens, o=o1, workspace=ws1, stream=stream)
+
+        for _ in range(3):
+            b1_call()
+        reps = 20
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        for _ in range(reps):
+            b1_call()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        ms = a_ev.elapsed_time(b_ev) / reps
+        by = c1.kv_bytes()
+        b1[name] = {"kv_bytes_per_call": by, "us_per_call": round(ms * 1e3, 2),
+                    "kv_GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del c1, o1, ws1
+    line["config"]["single_sequence_262144"] = b1
     line["config"]["prefill"] = bench_prefill(args.seed, dev, stream)
     log("measuring the plain read stream (4 GiB)")
     probes = hbm_probes(4 << 30)
