@@ -262,7 +262,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     const char* kb;
     const char* vb;
     int pos0;
-    bool ok;  // page id inside the pool
+    int ok;  // page id inside the pool (an int: the struct has no padding bytes,
+             // which the compiler would otherwise copy through LDS)
   };
   auto tile_at = [&](int it) {
     TileAt ta;
