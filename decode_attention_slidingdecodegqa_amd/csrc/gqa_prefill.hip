@@ -395,6 +395,12 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           auto kread = [&](int n) {
             return *reinterpret_cast<const u32x4*>(kt + (n / KCH) * 16 * RSK + (n % KCH) * 64);
           };
+          // the wave in its QK^T phase runs at a raised priority: the eight
+          // waves leave each step's barrier together, and the raised wave's
+          // MFMAs and key reads issue ahead of the other wave of its SIMD,
+          // which drifts into its softmax and PV products meanwhile
+          // (measured 3-7% faster on the global layer, 1-2% on the sliding)
+          __builtin_amdgcn_s_setprio(1);
           u32x4 kring[KDEPTH];
 #pragma unroll
           for (int n = 0; n < KDEPTH; ++n) kring[n] = kread(n);
@@ -419,6 +425,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
             __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
             if (n + KDEPTH < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
+          __builtin_amdgcn_s_setprio(0);
         } else {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
