@@ -161,6 +161,11 @@ def oracle_sample(sl_case, gl_case, n_sl, n_gl, threads):
     return nbytes, dt
 
 
+# untimed calls before each timed section after the step: the first calls
+# after a switch of workload run measurably slower
+SECTION_WARMUP = 10
+
+
 def bench_prefill(seed, dev, stream) -> dict:
     """Times each prefill workload: the call with stream events, the kernel with
     the library's own HIP events on the launch stream; the algorithmic flops
@@ -180,8 +185,7 @@ def bench_prefill(seed, dev, stream) -> dict:
             fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
                stream=stream)
 
-        # ten untimed calls: the first few after a switch of workload run slow
-        for _ in range(10):
+        for _ in range(SECTION_WARMUP):
             pf_call()
         reps = 10
         gqa.profile_begin(reps + 2)
@@ -349,7 +353,7 @@ def main():
     for W in SWEEP_WINDOWS:
         need = gqa.gqa_decode_workspace_bytes("sliding", sl.B, sl.cap, window=W)
         ws_w = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        for _ in range(2):
+        for _ in range(SECTION_WARMUP):
             gqa.gqa_decode_sliding_window(sl.q, sl.k, sl.v, sl.seq_lens, W, o=o_sl,
                                           workspace=ws_w, stream=stream)
         a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -386,7 +390,7 @@ def main():
             call = lambda: gqa.gqa_append_global(tok[0], tok[1], wq, wk, case.seq_lens, case.k,
                                                  case.v, block_table=case.block_table,
                                                  q_out=q_out, stream=stream)
-        for _ in range(3):
+        for _ in range(SECTION_WARMUP):
             call()
         a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 20
@@ -408,7 +412,7 @@ def main():
         gqa.gqa_decode_global_k_eq_v_paged(gl.q, gl.v, gl.w_k, gl.block_table, gl.seq_lens,
                                            o=o_kv, workspace=ws_gl, stream=stream)
 
-    for _ in range(2):
+    for _ in range(SECTION_WARMUP):
         kfv_call()
     reps = max(3, min(args.steps, 10))
     gqa.profile_begin(2 * reps + 4)
@@ -446,7 +450,7 @@ def main():
         gqa.gqa_decode_sliding_ring(rg.q, rg.k, rg.v, rg.seq_lens, window=1024, o=o_rg,
                                     workspace=ws_rg, stream=stream)
 
-    for _ in range(2):
+    for _ in range(SECTION_WARMUP):
         ring_call()
     reps = max(3, min(args.steps, 10))
     a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -475,7 +479,7 @@ def main():
         def b1_call():
             fn1(c1.q, c1.k, c1.v, c1.block_table, c1.seq_lens, o=o1, workspace=ws1, stream=stream)
 
-        for _ in range(3):
+        for _ in range(SECTION_WARMUP):
             b1_call()
         reps = 20
         a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
