@@ -796,49 +796,81 @@ struct CombineArgs {
   int32_t n_waves;
 };
 
-// One work-group of kCombineWaves waves per (sequence, query head).  Wave w
-// merges the partials w, w + kCombineWaves, ... of the unit (lane l owns
-// d = (D/64) l .. (D/64)(l+1) - 1, U partials in flight), then the waves'
-// sums are added in LDS in wave order.  A unit held by one slice was written
-// by its wave; a sequence with nothing attended gets a zero row.  With few
-// sequences a unit spans hundreds of slices, so the waves' loads in flight
-// set the combine's time.
+// One work-group of kCombineWaves waves per (sequence, query head, d part):
+// the head's D values are cut into DS parts of D/DS (DS > 1 when there are
+// few sequences, so that more work-groups share the reads).  Wave w merges the
+// partials w, w + kCombineWaves, ... of the unit: lane l owns PER = D/(64 DS)
+// consecutive d values of the part, with U partials in flight (more for
+// narrower lanes).  The waves' sums are then added in LDS in wave order.  The
+// first batch of partial rows is loaded together with the (m, l) pairs the
+// reference max needs, since those loads do not depend on it.  A unit held by
+// one slice was written by its wave; a sequence with nothing attended gets a
+// zero row.
 constexpr int kCombineWaves = 8;
 
-template <int KV, int D, bool BF16>
+// PER consecutive floats at p (16-, 8- or 4-byte aligned as PER asks)
+template <int PER>
+__device__ __forceinline__ void load_floats(const float* p, float (&v)[PER]) {
+  if constexpr (PER % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * c + e] = t[e];
+    }
+  } else if constexpr (PER == 2) {
+    const f32x2 t = *reinterpret_cast<const f32x2*>(p);
+    v[0] = t[0];
+    v[1] = t[1];
+  } else {
+    static_assert(PER == 1, "lane width");
+    v[0] = *p;
+  }
+}
+
+template <int KV, int D, bool BF16, int DS>
 __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(CombineArgs a) {
   constexpr int G = kHeads / KV;
   constexpr int EB = Elem<BF16>::bytes;
-  constexpr int PER = D / 64;  // d values per lane
-  constexpr int NV = PER / 4;  // 16-byte chunks per lane
-  constexpr int U = 8;         // partials in flight per lane
-  __shared__ __attribute__((aligned(16))) float s_acc[kCombineWaves][D];
+  constexpr int DW = D / DS;   // d values of this work-group
+  constexpr int PER = DW / 64;  // d values per lane
+  static_assert(PER == 1 || PER == 2 || PER % 4 == 0, "lane width");
+  // partials in flight per lane: a batch is one round trip, so narrow lanes
+  // take more of them (about 64 registers of partial rows either way)
+  constexpr int U = PER >= 4 ? 8 : 16;
+  __shared__ __attribute__((aligned(16))) float s_acc[kCombineWaves][DW];
   __shared__ float s_l[kCombineWaves];
-  const int b = blockIdx.x / kHeads;
-  const int h = blockIdx.x % kHeads;
+  const int bh = blockIdx.x / DS;
+  const int part = blockIdx.x % DS;
+  const int b = bh / kHeads;
+  const int h = bh % kHeads;
   const int g = h / G;
   const int hh = h % G;
   const int unit = b * KV + g;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int d = lane * PER;
+  const int dl = lane * PER;        // within the part
+  const int d = part * DW + dl;     // within the head row
   char* dst = a.o + ((size_t)b * kHeads + h) * D * EB + (size_t)d * EB;
 
   auto store = [&](const float (&run)[PER]) {
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      if constexpr (BF16) {
-        *reinterpret_cast<u32x2*>(dst + 4 * c * EB) =
-            u32x2{bf16_pack2(run[4 * c], run[4 * c + 1]), bf16_pack2(run[4 * c + 2], run[4 * c + 3])};
+    if constexpr (BF16) {
+      if constexpr (PER == 1) {
+        *reinterpret_cast<unsigned short*>(dst) = (unsigned short)(bf16_pack2(run[0], 0.f) & 0xffffu);
       } else {
-        *reinterpret_cast<f32x4*>(dst + 4 * c * EB) =
-            f32x4{run[4 * c], run[4 * c + 1], run[4 * c + 2], run[4 * c + 3]};
+#pragma unroll
+        for (int c = 0; c < PER; c += 2)
+          *reinterpret_cast<unsigned*>(dst + c * EB) = bf16_pack2(run[c], run[c + 1]);
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < PER; ++c) *reinterpret_cast<float*>(dst + c * EB) = run[c];
     }
   };
 
   const int P0 = a.prefix[b];
   const int n = (a.prefix[b + 1] - P0) / KV;
+  const long T = a.prefix[a.B];
   if (n <= 0) {
     if (wave == 0) {
       float zero[PER];
@@ -848,7 +880,6 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
     }
     return;
   }
-  const long T = a.prefix[a.B];
   const long s0 = P0 + (long)g * n;
   const int wf = wave_of(s0, T, a.n_waves);
   const int wl = wave_of(s0 + n - 1, T, a.n_waves);
@@ -858,70 +889,92 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
   const float* accp = a.ws_acc + (((size_t)unit + wf) * G + hh) * D + d;
   const size_t sstride = (size_t)G * D;
   // waves between wf and wl whose slices are empty (more waves than tiles)
-  // wrote nothing: their slots are skipped
+  // wrote nothing: their slots are skipped.  With at least as many tiles as
+  // waves every slice holds a tile; otherwise slice w = [wT/W, (w+1)T/W) is
+  // tested with double divisions, exact here: (w+1)T < 2^53 is exact, the
+  // quotient is correctly rounded, and a quotient that is not an integer lies
+  // at least 1/W from one
+  const bool all_hold = T >= a.n_waves;
+  const double Td = (double)T, Wd = (double)a.n_waves;
   auto holds = [&](int s) {
-    const long w = wf + s;
-    return (w + 1) * T / a.n_waves > w * T / a.n_waves;
+    if (all_hold) return true;
+    const double w = (double)(wf + s);
+    return floor((w + 1.0) * Td / Wd) > floor(w * Td / Wd);
   };
-  // the reference max over the partials, lane-parallel in every wave
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) {
-    if (!holds(s)) continue;
-    const f32x2 x = ml[(size_t)s * G];
-    if (x[1] > 0.f) M = fmaxf(M, x[0]);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-  f32x4 A[NV];
-#pragma unroll
-  for (int c = 0; c < NV; ++c) A[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float Lt = 0.f;
-  for (int s0u = wave; s0u < ns; s0u += kCombineWaves * U) {
-    f32x4 x[U][NV];
-    float wgt[U];
+  float x[U][PER];
+  f32x2 e[U];
+  bool okb[U];
+  auto load_batch = [&](int s0u) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int su = s0u + kCombineWaves * u;
       const int s = su < ns ? su : ns - 1;
-      const f32x2 e = ml[(size_t)s * G];
-      const bool ok = su < ns && holds(s) && e[1] > 0.f;
-      wgt[u] = ok ? exp2_fast((e[0] - M) * kLog2e) : 0.f;
-      Lt += wgt[u] * (ok ? e[1] : 0.f);
-#pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        x[u][c] = *reinterpret_cast<const f32x4*>(accp + (size_t)s * sstride + 4 * c);
-        x[u][c] = ok ? x[u][c] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      e[u] = ml[(size_t)s * G];
+      okb[u] = su < ns && holds(s);
+      load_floats<PER>(accp + (size_t)s * sstride, x[u]);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NV; ++c) A[c] += wgt[u] * x[u][c];
+  };
+  load_batch(wave);
+
+  // the reference max over the partials, lane-parallel in every wave
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) {
+    if (!holds(s)) continue;
+    const f32x2 y = ml[(size_t)s * G];
+    if (y[1] > 0.f) M = fmaxf(M, y[0]);
   }
 #pragma unroll
-  for (int c = 0; c < NV; ++c) *reinterpret_cast<f32x4*>(&s_acc[wave][d + 4 * c]) = A[c];
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float A[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) A[i] = 0.f;
+  float Lt = 0.f;
+  auto accumulate = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // a slot nothing wrote may hold anything: select, never multiply by 0
+      const bool ok = okb[u] && e[u][1] > 0.f;
+      const float wgt = ok ? exp2_fast((e[u][0] - M) * kLog2e) : 0.f;
+      Lt += ok ? wgt * e[u][1] : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) A[i] += ok ? wgt * x[u][i] : 0.f;
+    }
+  };
+  accumulate();
+  for (int s0u = wave + kCombineWaves * U; s0u < ns; s0u += kCombineWaves * U) {
+    load_batch(s0u);
+    accumulate();
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s_acc[wave][dl + i] = A[i];
   if (lane == 0) s_l[wave] = Lt;
   __syncthreads();
   if (wave != 0) return;
   float L = 0.f;
   float run[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) run[e] = 0.f;
+  for (int i = 0; i < PER; ++i) run[i] = 0.f;
 #pragma unroll
   for (int w = 0; w < kCombineWaves; ++w) {
     L += s_l[w];
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&s_acc[w][d + 4 * c]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) run[4 * c + e] += v[e];
-    }
+    for (int i = 0; i < PER; ++i) run[i] += s_acc[w][dl + i];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) run[e] = L > 0.f ? run[e] * inv : 0.f;
+  for (int i = 0; i < PER; ++i) run[i] = L > 0.f ? run[i] * inv : 0.f;
   store(run);
+}
+
+// d parts per (sequence, head) of the combine: enough work-groups to spread
+// the partial reads (at least 1024 when D allows it; one lane per d at most)
+template <int D>
+inline int combine_parts(int B) {
+  int ds = 1;
+  while (ds < D / 64 && (long)B * kHeads * ds < 1024) ds *= 2;
+  return ds;
 }
 
 // ------------------------------------------------------------- KV append
@@ -1220,9 +1273,21 @@ MainFn pick_main(bool unit_mode, bool paged, bool bf16) {
   return bf16 ? gqa_stream_kernel<KV, D, false, true, KFV> : gqa_stream_kernel<KV, D, false, false, KFV>;
 }
 
+template <int KV, int D, int DS>
+CombineFn pick_combine_ds(bool bf16) {
+  return bf16 ? gqa_combine_kernel<KV, D, true, DS> : gqa_combine_kernel<KV, D, false, DS>;
+}
+
 template <int KV, int D>
-CombineFn pick_combine(bool bf16) {
-  return bf16 ? gqa_combine_kernel<KV, D, true> : gqa_combine_kernel<KV, D, false>;
+CombineFn pick_combine(bool bf16, int ds) {
+  switch (ds) {
+    case 1: return pick_combine_ds<KV, D, 1>(bf16);
+    case 2: return pick_combine_ds<KV, D, 2>(bf16);
+    case 4: return pick_combine_ds<KV, D, 4>(bf16);
+    default:
+      if constexpr (D / 64 >= 8) return pick_combine_ds<KV, D, 8>(bf16);
+      return nullptr;
+  }
 }
 
 inline int default_window(int variant) { return variant == GQA_SLIDING ? kSlidingWindow : 0; }
@@ -1309,11 +1374,14 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ca.o = ka.o;
   ca.B = B;
   ca.n_waves = plan.waves;
+  const int ds = variant == GQA_SLIDING ? combine_parts<256>(B) : combine_parts<512>(B);
   CombineFn comb =
-      variant == GQA_SLIDING ? pick_combine<16, 256>(bf16) : pick_combine<4, 512>(bf16);
+      variant == GQA_SLIDING ? pick_combine<16, 256>(bf16, ds) : pick_combine<4, 512>(bf16, ds);
+  if (!comb) return GQA_ERR_SHAPE;
   ProfRec* pc = prof_slot(kfv ? kProfKeysFromValues + 1 : 2 * variant + 1);
   if (pc) hipEventRecord(pc->start, stream);
-  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads)), dim3(64u * kCombineWaves), 0, stream, ca);
+  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads * ds)), dim3(64u * kCombineWaves), 0, stream,
+                     ca);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (pc) hipEventRecord(pc->stop, stream);
   return GQA_OK;
