@@ -55,6 +55,21 @@ def test_parity_batch_shapes(variant):
         assert err <= TOL["bf16"], (B, cap, err)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_combine_d_parts(variant, dtype):
+    # stream mode at batch sizes that give the combine 8, 4, 2 and 1 d parts per head
+    # (fewer than 1024 (sequence, head) rows split each head's D across work-groups)
+    cap = SMALL[variant][0]
+    for B in ((1, 2, 5, 16, 24, 31, 33) if dtype == "bf16" else (1, 16, 33)):
+        assert gqa.gqa_decode_plan(variant, B, cap)["mode"] == "stream"
+        lens = synth.draw_seq_lens(("uniform", 1, cap), B, 200 + B)
+        lens[0] = cap
+        c = synth.make_case(variant, dtype, B, cap, lens, seed=200 + B)
+        err = max_err(to_f64(hip_run(to_gpu(c))), oracle_run(c))
+        assert err <= TOL[dtype], (variant, dtype, B, err)
+
+
 UNIT_MODE = {"sliding": (64, 1104), "global": (256, 512)}  # B, capacity
 
 
