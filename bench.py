@@ -489,10 +489,27 @@ def main():
         b_ev.record(stream)
         torch.cuda.synchronize()
         ms = a_ev.elapsed_time(b_ev) / reps
+        # single calls, each after a 2 GiB write that evicts the caches (the
+        # sliding window is 16 MiB): the median of 50, outside any warm chain
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        single = []
+        for _ in range(50):
+            flush.fill_(1)
+            torch.cuda.synchronize()
+            a_ev.record(stream)
+            b1_call()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            single.append(a_ev.elapsed_time(b_ev))
+        del flush
+        single.sort()
+        ms_cold = single[len(single) // 2]
         by = c1.kv_bytes()
         b1[name] = {"kv_bytes_per_call": by, "us_per_call": round(ms * 1e3, 2),
                     "kv_GBps": round(by / (ms * 1e-3) / 1e9, 1),
-                    "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "us_per_call_after_flush_median": round(ms_cold * 1e3, 2),
+                    "frac_of_hbm_peak_after_flush": round(by / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del c1, o1, ws1
     line["config"]["single_sequence_262144"] = b1
     line["config"]["prefill"] = bench_prefill(args.seed, dev, stream)
