@@ -467,7 +467,7 @@ def main():
         "us_per_call": round(ms * 1e3, 2), "kv_GBps": round(rg_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(rg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del rg, o_rg, ws_rg
-    log("one sequence of 262144 positions (paged), both geometries")
+    log("one sequence of 262144 positions (paged), both geometries; also cold single calls")
     b1 = {}
     for name in ("global_bf16_b1_paged_s262144", "sliding_bf16_b1_paged_s262144"):
         c1 = synth.make_workload(name, seed=args.seed, device=dev, fill=0.0)
@@ -489,12 +489,13 @@ def main():
         b_ev.record(stream)
         torch.cuda.synchronize()
         ms = a_ev.elapsed_time(b_ev) / reps
-        # single calls, each after a 2 GiB write that evicts the caches (the
-        # sliding window is 16 MiB): the median of 50, outside any warm chain
-        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        # single calls, each after a 2 GiB read that evicts the caches (the
+        # sliding window is 16 MiB): the median of 50, outside any warm chain.
+        # A read leaves no dirty lines for the call to write back.
+        flush = torch.ones(512 << 20, dtype=torch.float32, device=dev)
         single = []
         for _ in range(50):
-            flush.fill_(1)
+            flush.sum()
             torch.cuda.synchronize()
             a_ev.record(stream)
             b1_call()
