@@ -376,7 +376,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     }
     w_lo = __builtin_amdgcn_readfirstlane(w_lo);
     w_hi = __builtin_amdgcn_readfirstlane(w_hi);
-    auto compute = [&](int step, int ok_cur, auto& cur) {
+    auto compute = [&](int step, int ok_cur, auto& cur, auto&& after_qk) {
         const char* kt = cur + kbase;
         const char* vt = cur + vbase;
         // logits z[cb][h][key 16h+4j+i][column r of block cb]; each K operand
@@ -455,6 +455,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           for (int cb = 0; cb < CB; ++cb) z[cb][h] = z0[cb] + z1[cb];
         }
         }
+        after_qk();
         // each column keeps the keys of its own mask; online softmax per block
         const int pos0 = step * PT;
         float p[CB][NH][4];
@@ -558,15 +559,24 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
 
     // one step: fetch the next one into the other buffer, compute on this one,
     // publish the next (one barrier per step); the loop takes steps in pairs so
-    // that each buffer is named statically
+    // that each buffer is named statically.  The LDS-DMA fetch is issued after
+    // the QK^T products: its LDS writes then meet the softmax and PV instead of
+    // the key reads every wave issues at the start of the step (measured 3%
+    // faster on the global layer); the register-staged fetch is issued first
     int ok_cur, ok_nxt = 0;
     fetch(step_begin, ok_cur, s_kv0);
     stash(s_kv0);
     __syncthreads();
     auto one_step = [&](int step, auto& cur, auto& nxt) {
       const bool more = step < step_end;
-      if (more) fetch(step + 1, ok_nxt, nxt);
-      if (wave_live) compute(step, ok_cur, cur);
+      if (!DMA && more) fetch(step + 1, ok_nxt, nxt);
+      auto fetch_dma = [&] {
+        if constexpr (DMA) {
+          if (more) fetch(step + 1, ok_nxt, nxt);
+        }
+      };
+      if (wave_live) compute(step, ok_cur, cur, fetch_dma);
+      else fetch_dma();
       if (more) stash(nxt);
       __syncthreads();
       ok_cur = ok_nxt;
