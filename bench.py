@@ -324,6 +324,34 @@ def main():
             "plan": plan_gl,
         },
     }
+    # each call also timed on its own (events around one call, the stream
+    # drained in between): the median of 50, after the timed steps above
+    def median_single(call, n=50):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = []
+        for _ in range(n):
+            a_ev.record(stream)
+            call()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            t.append(a_ev.elapsed_time(b_ev))
+        t.sort()
+        return t[len(t) // 2]
+
+    for name, call, nb in (
+            ("sliding", lambda: gqa.gqa_decode_sliding(sl.q, sl.k, sl.v, sl.seq_lens, o=o_sl,
+                                                       workspace=ws_sl, stream=stream), sl_bytes),
+            ("global", lambda: gqa.gqa_decode_global_paged(gl.q, gl.k, gl.v, gl.block_table,
+                                                           gl.seq_lens, o=o_gl, workspace=ws_gl,
+                                                           stream=stream), gl_bytes)):
+        med = median_single(call)
+        config[name]["us_per_call_median_of_50_single"] = round(med * 1e3, 2)
+        config[name]["frac_of_hbm_peak_median_single"] = round(
+            nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    log("single-call medians: sliding %.1f us, global %.1f us" % (
+        config["sliding"]["us_per_call_median_of_50_single"],
+        config["global"]["us_per_call_median_of_50_single"]))
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
