@@ -423,6 +423,14 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
+  // bf16 keys from values: the query operand is the same for every tile of the
+  // unit, so it is read from LDS once into registers
+  u32x4 qreg[STAGED ? KCH : 1];
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) qreg[c] = qrow[(4 * c + j) ^ qswz];
+  }
+
   for (int it = 0; it < n_it; ++it) {
     const bool more = it + 1 < n_it;
     const TileAt nxt = more ? tile_at(it + 1) : cur;
@@ -453,9 +461,14 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
           // columns >= G: zero (stored-key kernels, HBM-bound: a branch around
           // the read costs nothing and the registers are full) or head 0
           // (keys from values, compute-bound)
-          const u32x4 q0 = KFV || r < G ? qrow[(4 * c + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
-          const u32x4 q1 =
-              KFV || r < G ? qrow[(4 * c + 4 + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
+          u32x4 q0, q1;
+          if constexpr (STAGED) {
+            q0 = qreg[c];
+            q1 = qreg[c + 1];
+          } else {
+            q0 = KFV || r < G ? qrow[(4 * c + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
+            q1 = KFV || r < G ? qrow[(4 * c + 4 + j) ^ qswz] : u32x4{0u, 0u, 0u, 0u};
+          }
           z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c)),
                                                        __builtin_bit_cast(bf16x8, q0), z0, 0, 0, 0);
           z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, key_op(c + 1)),
