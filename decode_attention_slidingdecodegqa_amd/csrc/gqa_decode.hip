@@ -1234,7 +1234,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   [prefix: B+1 int32][ml: slots x G x 2 fp32][acc: slots x G x D fp32],
 // slots = B*KV + W (a slice's partial of unit u sits in slot u + wave).
 constexpr int kUnitModeMinUnits = 1024;
-constexpr int kUnitModeMaxTiles = 128;
+// 320: at B=256, unit mode measured faster up to 257 tiles per unit (sliding
+// windows 2048 and 4096: 1,058 vs 1,105 and 1,791 vs 1,826 us; global with a
+// 4096-position cache: 707 vs 722 us) and slower at 512 (window 8192 and a
+// 8192-position global cache: 2,481 vs 2,462 and 1,495 vs 1,423 us)
+constexpr int kUnitModeMaxTiles = 320;
 
 struct Plan {
   int mode;  // GQA_MODE_UNIT or GQA_MODE_STREAM

@@ -280,7 +280,7 @@ enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1 };
 
 /* The launch plan for these arguments (a function of them alone).
  * GQA_MODE_UNIT: one work-group of four waves per (sequence, kv head), used
- *   when there are at least 1024 such units of at most 128 tiles of 16
+ *   when there are at least 1024 such units of at most 320 tiles of 16
  *   positions; no workspace; *n_waves = 4 * units, *n_slots = 0.
  * GQA_MODE_STREAM: *n_waves persistent waves each take an equal share of all
  *   tiles, partials of units shared by several waves go to *n_slots workspace

@@ -64,7 +64,7 @@ def test_plan_and_workspace(lib, variant, B, cap):
     if variant == "sliding":
         tiles = min(tiles, 1024 // 16 + 1)
     ws = gqa.gqa_decode_workspace_bytes(variant, B, cap)
-    if B * KV >= 1024 and tiles <= 128:
+    if B * KV >= 1024 and tiles <= 320:
         # many short units: one work-group of four waves per unit, no workspace
         assert plan == {"mode": "unit", "waves": 4 * B * KV, "slots": 0}
         assert ws == 0

@@ -270,11 +270,12 @@ def test_window_parity(window, paged):
     assert err <= TOL["bf16"], (window, paged, err)
 
 
-@pytest.mark.parametrize("window", [512, 2048])
-def test_window_parity_unit_mode_and_f32(window):
-    B, cap = 64, 4096
+@pytest.mark.parametrize("window,B,expect", [(512, 64, "unit"), (2048, 64, "unit"),
+                                             (2048, 32, "stream")])
+def test_window_parity_unit_mode_and_f32(window, B, expect):
+    cap = 4096
     mode = gqa.gqa_decode_plan("sliding", B, cap, window=window)["mode"]
-    assert mode == ("unit" if window == 512 else "stream")
+    assert mode == expect
     lens = synth.draw_seq_lens(("uniform", 1, cap), B, 9)
     c = synth.make_case("sliding", "f32", B, cap, lens, seed=121, window=window)
     err = max_err(to_f64(hip_run(to_gpu(c), window=window)), oracle_run(c, window=window))
