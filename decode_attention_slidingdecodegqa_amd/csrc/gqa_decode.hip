@@ -1227,18 +1227,34 @@ __global__ __launch_bounds__(256) void hbm_copy_kernel(const u32x4* src, u32x4* 
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Launch plan, a function of (variant, B, capacity) only.  Many short units
-// (at least kUnitModeMinUnits units of at most kUnitModeMaxTiles tiles) fill
-// the GPU one work-group per unit and need no workspace; otherwise the stream
-// partition runs with workspace
+// Launch plan, a function of (variant, B, capacity) only.  Enough short units
+// fill the GPU one work-group per unit and need no workspace; otherwise the
+// stream partition runs with workspace
 //   [prefix: B+1 int32][ml: slots x G x 2 fp32][acc: slots x G x D fp32],
 // slots = B*KV + W (a slice's partial of unit u sits in slot u + wave).
+//
+// Unit mode's time is set by its longest unit (a quarter of its tiles per
+// wave, one after another), stream mode's by the bytes plus a combine, so
+// unit mode needs more units the longer they are.  The tiers are measured
+// (B uniform lengths, bf16):
+//   - up to 320 tiles, from 1024 units: sliding windows 2048 / 4096 at B=256,
+//     1,058 vs 1,105 and 1,791 vs 1,826 us; a 4096-position global cache at
+//     B=256, 707 vs 722 us.  At 512 tiles it loses (window 8192: 2,481 vs
+//     2,462; an 8192-position global cache: 1,495 vs 1,423 us), and at 256
+//     tiles with 512 or 768 units it loses 3%;
+//   - up to 128 tiles, from 256 units: global B=64 with a 2048-position
+//     cache, 106 vs 113 us; sliding B=16, 37 vs 51 us.  Global B=32 with 128
+//     tiles loses (87 vs 60 us);
+//   - sliding geometry only, up to 65 tiles (one window), from 128 units:
+//     sliding B=8, 27 vs 37 us.  Sliding B <= 4 loses (25 vs 16-23 us), and so
+//     does global B=32 with a 1024-position cache (48.5 vs 43.8 us: its tiles
+//     are twice the bytes, at one wave per SIMD).
 constexpr int kUnitModeMinUnits = 1024;
-// 320: at B=256, unit mode measured faster up to 257 tiles per unit (sliding
-// windows 2048 and 4096: 1,058 vs 1,105 and 1,791 vs 1,826 us; global with a
-// 4096-position cache: 707 vs 722 us) and slower at 512 (window 8192 and a
-// 8192-position global cache: 2,481 vs 2,462 and 1,495 vs 1,423 us)
 constexpr int kUnitModeMaxTiles = 320;
+inline bool unit_mode_fits(int units, int tiles_max, int D) {
+  return (units >= kUnitModeMinUnits && tiles_max <= kUnitModeMaxTiles) ||
+         (units >= 256 && tiles_max <= 128) || (D == 256 && units >= 128 && tiles_max <= 65);
+}
 
 struct Plan {
   int mode;  // GQA_MODE_UNIT or GQA_MODE_STREAM
@@ -1259,7 +1275,7 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   }
   const int units = B * vi.KV;
   *P = Plan{};
-  if (units >= kUnitModeMinUnits && tiles_max <= kUnitModeMaxTiles) {
+  if (unit_mode_fits(units, tiles_max, vi.D)) {
     P->mode = GQA_MODE_UNIT;
     P->waves = units * kWaves;
     return GQA_OK;

@@ -280,8 +280,10 @@ enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1 };
 
 /* The launch plan for these arguments (a function of them alone).
  * GQA_MODE_UNIT: one work-group of four waves per (sequence, kv head), used
- *   when there are at least 1024 such units of at most 320 tiles of 16
- *   positions; no workspace; *n_waves = 4 * units, *n_slots = 0.
+ *   when there are enough such units for their length (at least 1024 units
+ *   of at most 320 tiles of 16 positions, 256 of at most 128, or on the
+ *   sliding geometry 128 of at most 65); no workspace; *n_waves = 4 * units,
+ *   *n_slots = 0.
  * GQA_MODE_STREAM: *n_waves persistent waves each take an equal share of all
  *   tiles, partials of units shared by several waves go to *n_slots workspace
  *   slots, and a combine kernel merges them.

@@ -55,7 +55,8 @@ def test_constants_match_pages(lib):
 
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 @pytest.mark.parametrize("B,cap", [(1, 1), (1, 262144), (4, 2048), (4, 4096), (32, 131072),
-                                   (256, 8192), (256, 262144), (7, 33)])
+                                   (256, 8192), (256, 262144), (7, 33), (8, 8192), (32, 1024),
+                                   (64, 2048), (128, 4096), (256, 4096)])
 def test_plan_and_workspace(lib, variant, B, cap):
     plan = gqa.gqa_decode_plan(variant, B, cap)
     KV = 16 if variant == "sliding" else 4
@@ -64,7 +65,9 @@ def test_plan_and_workspace(lib, variant, B, cap):
     if variant == "sliding":
         tiles = min(tiles, 1024 // 16 + 1)
     ws = gqa.gqa_decode_workspace_bytes(variant, B, cap)
-    if B * KV >= 1024 and tiles <= 320:
+    units = B * KV
+    if (units >= 1024 and tiles <= 320) or (units >= 256 and tiles <= 128) or \
+            (D == 256 and units >= 128 and tiles <= 65):
         # many short units: one work-group of four waves per unit, no workspace
         assert plan == {"mode": "unit", "waves": 4 * B * KV, "slots": 0}
         assert ws == 0

@@ -59,14 +59,16 @@ def test_parity_batch_shapes(variant):
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 def test_combine_d_parts(variant, dtype):
     # stream mode at batch sizes that give the combine 8, 4, 2 and 1 d parts per head
-    # (fewer than 1024 (sequence, head) rows split each head's D across work-groups)
+    # (fewer than 1024 (sequence, head) rows split each head's D across work-groups);
+    # sliding with a 2048 window, whose 129-tile units keep these batches in stream mode
     cap = SMALL[variant][0]
+    window = 2048 if variant == "sliding" else None
     for B in ((1, 2, 5, 16, 24, 31, 33) if dtype == "bf16" else (1, 16, 33)):
-        assert gqa.gqa_decode_plan(variant, B, cap)["mode"] == "stream"
+        assert gqa.gqa_decode_plan(variant, B, cap, window=window)["mode"] == "stream"
         lens = synth.draw_seq_lens(("uniform", 1, cap), B, 200 + B)
         lens[0] = cap
-        c = synth.make_case(variant, dtype, B, cap, lens, seed=200 + B)
-        err = max_err(to_f64(hip_run(to_gpu(c))), oracle_run(c))
+        c = synth.make_case(variant, dtype, B, cap, lens, seed=200 + B, window=window)
+        err = max_err(to_f64(hip_run(to_gpu(c), window=window)), oracle_run(c, window=window))
         assert err <= TOL[dtype], (variant, dtype, B, err)
 
 
