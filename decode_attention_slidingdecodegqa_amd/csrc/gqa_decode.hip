@@ -1410,10 +1410,10 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
                    : kfv                   ? pick_main<4, 512, true>(unit_mode, paged, bf16)
                                            : pick_main<4, 512, false>(unit_mode, paged, bf16);
   ProfRec* pr = prof_slot(kfv ? kProfKeysFromValues : 2 * variant);
-  if (pr) hipEventRecord(pr->start, stream);
+  if (pr) (void)hipEventRecord(pr->start, stream);
   hipLaunchKernelGGL(main_fn, dim3((unsigned)(plan.waves / kWaves)), dim3(kThreads), 0, stream, ka);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
-  if (pr) hipEventRecord(pr->stop, stream);
+  if (pr) (void)hipEventRecord(pr->stop, stream);
   if (unit_mode) return GQA_OK;
 
   CombineArgs ca;
@@ -1428,11 +1428,11 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
       variant == GQA_SLIDING ? pick_combine<16, 256>(bf16, ds) : pick_combine<4, 512>(bf16, ds);
   if (!comb) return GQA_ERR_SHAPE;
   ProfRec* pc = prof_slot(kfv ? kProfKeysFromValues + 1 : 2 * variant + 1);
-  if (pc) hipEventRecord(pc->start, stream);
+  if (pc) (void)hipEventRecord(pc->start, stream);
   hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads * ds)), dim3(64u * kCombineWaves), 0, stream,
                      ca);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
-  if (pc) hipEventRecord(pc->stop, stream);
+  if (pc) (void)hipEventRecord(pc->stop, stream);
   return GQA_OK;
 }
 
@@ -1496,12 +1496,12 @@ int run_append(int variant, bool paged, bool values_only, const void* q_raw, con
   AppendFn fn = global ? pick_append<4, 512>(paged, bf16) : pick_append<16, 256>(paged, bf16);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   ProfRec* pr = prof_slot(values_only ? kProfKeysFromValues + 2 : 4 + variant);
-  if (pr) hipEventRecord(pr->start, stream);
+  if (pr) (void)hipEventRecord(pr->start, stream);
   const unsigned rows = kHeads + 2 * (global ? 4 : 16);  // q, k and v head rows
   hipLaunchKernelGGL(fn, dim3((unsigned)B, (rows + kWaves - 1) / kWaves), dim3(kThreads), 0, stream,
                      aa);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
-  if (pr) hipEventRecord(pr->stop, stream);
+  if (pr) (void)hipEventRecord(pr->stop, stream);
   return GQA_OK;
 }
 
@@ -1512,11 +1512,11 @@ int prof_begin(int kind, hipStream_t stream) {
   if (!g_prof_on || g_prof_used >= g_prof.size()) return -1;
   const int slot = (int)g_prof_used++;
   g_prof[slot].kind = kind;
-  hipEventRecord(g_prof[slot].start, stream);
+  (void)hipEventRecord(g_prof[slot].start, stream);
   return slot;
 }
 void prof_end(int slot, hipStream_t stream) {
-  if (slot >= 0) hipEventRecord(g_prof[slot].stop, stream);
+  if (slot >= 0) (void)hipEventRecord(g_prof[slot].stop, stream);
 }
 }  // namespace gqa_detail
 
@@ -1744,8 +1744,8 @@ int gqa_hbm_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
 
 int gqa_profile_begin(int32_t capacity) {
   for (auto& r : g_prof) {
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_prof.clear();
   g_prof_used = 0;
@@ -1780,8 +1780,8 @@ int gqa_profile_read(int32_t* counts, double* total_ms, int32_t n_kinds) {
     }
   }
   for (auto& r : g_prof) {
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_prof.clear();
   g_prof_used = 0;
