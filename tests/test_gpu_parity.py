@@ -4,7 +4,6 @@ Every case is seeded and synthetic (synth.py).  Tolerances: max-abs error 1e-4
 for float32 inputs, 2e-2 for bfloat16 inputs (unit-RMS values).  Invariants
 that the method makes exact are checked bit for bit.
 """
-import numpy as np
 import pytest
 import torch
 
