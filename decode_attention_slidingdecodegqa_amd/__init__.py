@@ -23,6 +23,7 @@ the library is missing or no GPU is present the calls raise.
     gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache[, block_table])
     gqa_prefill_sliding(q, k, v, cu_q, seq_lens[, block_table])   prefill / chunked prefill
     gqa_prefill_global(q, k, v, cu_q, seq_lens[, block_table])
+    gqa_prefill_sliding_window(q, k, v, cu_q, seq_lens, window[, block_table])
 
 Shapes (attn.core of the gemma-4-31B Model Spec page): q [B,32,D]; contiguous
 k/v [B,S_max,KV,D]; paged pools [num_pages,16,KV,D] with block_table
@@ -59,6 +60,7 @@ from ._lib import (  # noqa: F401
     gqa_decode_workspace_bytes,
     gqa_prefill_global,
     gqa_prefill_sliding,
+    gqa_prefill_sliding_window,
     gqa_status_str,
     hbm_copy_probe,
     hbm_read_probe,

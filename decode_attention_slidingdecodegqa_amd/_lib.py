@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "gqa_append_global_k_eq_v_paged", "gqa_prefill_sliding", "gqa_prefill_global",
     "gqa_prefill_sliding_paged", "gqa_prefill_global_paged", "gqa_decode_sliding_ring",
     "gqa_decode_sliding_ring_workspace_bytes", "gqa_append_sliding_ring",
+    "gqa_prefill_sliding_window", "gqa_prefill_sliding_window_paged",
 )
 
 
@@ -84,6 +85,11 @@ def library():
     for name in ("gqa_prefill_sliding_paged", "gqa_prefill_global_paged"):
         getattr(lib, name).argtypes = [p, p, p, p, i32, p, p, p, i32, i32, i32, i32, p]
         getattr(lib, name).restype = ctypes.c_int
+    lib.gqa_prefill_sliding_window.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, p]
+    lib.gqa_prefill_sliding_window.restype = ctypes.c_int
+    lib.gqa_prefill_sliding_window_paged.argtypes = [p, p, p, p, i32, p, p, p, i32, i32, i32, i32,
+                                                     i32, p]
+    lib.gqa_prefill_sliding_window_paged.restype = ctypes.c_int
     for name in ("gqa_append_sliding", "gqa_append_sliding_paged", "gqa_append_global",
                  "gqa_append_global_paged", "gqa_decode_global_k_eq_v",
                  "gqa_decode_global_k_eq_v_paged", "gqa_append_global_k_eq_v",
@@ -520,7 +526,7 @@ def gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache, block_ta
     return q_out
 
 
-def _prefill_call(variant, q, k, v, cu_q, seq_lens, block_table, o, stream):
+def _prefill_call(variant, q, k, v, cu_q, seq_lens, block_table, o, stream, window=None):
     KV = 16 if variant == GQA_SLIDING else 4
     D = 256 if variant == GQA_SLIDING else 512
     if q.dim() != 3 or q.shape[1:] != (HEADS, D):
@@ -543,21 +549,29 @@ def _prefill_call(variant, q, k, v, cu_q, seq_lens, block_table, o, stream):
     if block_table is None:
         if k.dim() != 4 or k.shape[0] != B or k.shape[2:] != (KV, D) or v.shape != k.shape:
             raise ValueError(f"k/v must be [B,S_max,{KV},{D}]")
-        name = f"gqa_prefill_{kind}"
-        rc = getattr(lib, name)(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_q, "cu_q"),
-                                _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N, k.shape[1],
-                                _dtype_code(q), st)
+        args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_q, "cu_q"),
+                _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N, k.shape[1]]
+        if window is None:
+            name = f"gqa_prefill_{kind}"
+            rc = getattr(lib, name)(*args, _dtype_code(q), st)
+        else:
+            name = "gqa_prefill_sliding_window"
+            rc = lib.gqa_prefill_sliding_window(*args, int(window), _dtype_code(q), st)
     else:
         if k.dim() != 4 or k.shape[1:] != (PAGE, KV, D) or v.shape != k.shape:
             raise ValueError(f"k_pool/v_pool must be [num_pages,16,{KV},{D}]")
         if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
                 block_table.shape[0] != B:
             raise ValueError("block_table must be int32 [B,max_pages]")
-        name = f"gqa_prefill_{kind}_paged"
-        rc = getattr(lib, name)(_dev(q, "q"), _dev(k, "k_pool"), _dev(v, "v_pool"),
-                                _dev(block_table, "block_table"), block_table.shape[1],
-                                _dev(cu_q, "cu_q"), _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N,
-                                k.shape[0], _dtype_code(q), st)
+        args = [_dev(q, "q"), _dev(k, "k_pool"), _dev(v, "v_pool"),
+                _dev(block_table, "block_table"), block_table.shape[1], _dev(cu_q, "cu_q"),
+                _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, N, k.shape[0]]
+        if window is None:
+            name = f"gqa_prefill_{kind}_paged"
+            rc = getattr(lib, name)(*args, _dtype_code(q), st)
+        else:
+            name = "gqa_prefill_sliding_window_paged"
+            rc = lib.gqa_prefill_sliding_window_paged(*args, int(window), _dtype_code(q), st)
     if rc:
         raise GqaError(name, rc)
     return o
@@ -573,3 +587,12 @@ def gqa_prefill_sliding(q, k, v, cu_q, seq_lens, block_table=None, o=None, strea
 def gqa_prefill_global(q, k, v, cu_q, seq_lens, block_table=None, o=None, stream=None):
     """Prefill of the global layers (q [N,32,512], full causal mask)."""
     return _prefill_call(GQA_GLOBAL, q, k, v, cu_q, seq_lens, block_table, o, stream)
+
+
+def gqa_prefill_sliding_window(q, k, v, cu_q, seq_lens, window, block_table=None, o=None,
+                               stream=None):
+    """Prefill of the sliding geometry with a runtime window (1 <= window <=
+    262144; the gqa_prefill_sliding_window[_paged] entry points), otherwise as
+    gqa_prefill_sliding."""
+    return _prefill_call(GQA_SLIDING, q, k, v, cu_q, seq_lens, block_table, o, stream,
+                         window=window)

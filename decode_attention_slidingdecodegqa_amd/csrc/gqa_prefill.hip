@@ -631,11 +631,15 @@ constexpr int kProfPrefill = 9;           // profiling kinds 9 (sliding), 10 (gl
 int run_prefill(int variant, bool paged, const void* q, const void* k, const void* v,
                 const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
                 const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
-                int32_t num_pages, int32_t dtype, void* stream_) {
+                int32_t num_pages, int32_t dtype, void* stream_, int32_t window = -1) {
   if (!q || !k || !v || !cu_q || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
   if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
   VariantInfo vi;
   if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
+  // window < 0: the variant's own (1024 sliding, none global); otherwise a
+  // runtime window of the sliding geometry
+  if (window >= 0 && (variant != GQA_SLIDING || window < 1 || window > kMaxSeq))
+    return GQA_ERR_SHAPE;
   if (B < 1 || B > kMaxBatch || N < 1 || N > kMaxPrefillRows) return GQA_ERR_SHAPE;
   int cap;
   if (paged) {
@@ -659,7 +663,7 @@ int run_prefill(int variant, bool paged, const void* q, const void* k, const voi
   pa.cap = cap;
   pa.max_pages = paged ? max_pages : 0;
   pa.num_pages = paged ? num_pages : 0;
-  pa.window = vi.window;
+  pa.window = window >= 0 ? window : vi.window;
   const bool bf16 = dtype == GQA_BF16;
   PrefillFn fn = variant == GQA_SLIDING ? pick_prefill<16, 256>(paged, bf16)
                                         : pick_prefill<4, 512>(paged, bf16);
@@ -714,6 +718,24 @@ int gqa_prefill_global_paged(const void* q, const void* k_pool, const void* v_po
                              int32_t num_pages, int32_t dtype, void* stream) {
   return run_prefill(GQA_GLOBAL, true, q, k_pool, v_pool, block_table, max_pages, cu_q, seq_lens,
                      o, B, N, 0, num_pages, dtype, stream);
+}
+
+int gqa_prefill_sliding_window(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                               const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                               int32_t S_max, int32_t window, int32_t dtype, void* stream) {
+  if (window < 1) return GQA_ERR_SHAPE;  // (negative is the internal "variant default")
+  return run_prefill(GQA_SLIDING, false, q, k, v, nullptr, 0, cu_q, seq_lens, o, B, N, S_max, 0,
+                     dtype, stream, window);
+}
+
+int gqa_prefill_sliding_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages,
+                                     const int32_t* cu_q, const int32_t* seq_lens, void* o,
+                                     int32_t B, int32_t N, int32_t num_pages, int32_t window,
+                                     int32_t dtype, void* stream) {
+  if (window < 1) return GQA_ERR_SHAPE;
+  return run_prefill(GQA_SLIDING, true, q, k_pool, v_pool, block_table, max_pages, cu_q,
+                     seq_lens, o, B, N, 0, num_pages, dtype, stream, window);
 }
 
 }  // extern "C"

@@ -269,6 +269,22 @@ int gqa_prefill_global_paged(const void* q, const void* k_pool, const void* v_po
                              const int32_t* seq_lens, void* o, int32_t B, int32_t N,
                              int32_t num_pages, int32_t dtype, void* stream);
 
+/* Prefill of the sliding geometry with a runtime window: each query row at
+ * position p attends to [max(0, p - window + 1), p].  These are the per-layer
+ * windows of the Retrofit Plan page ("Progressive Window Assignment": 1024,
+ * 2048, 4096 and 8192 in the four sliding layers of a block); any
+ * 1 <= window <= 262144 is accepted (GQA_ERR_SHAPE otherwise).  Arguments,
+ * layouts and errors are those of gqa_prefill_sliding / _paged; window 1024
+ * is the default entry points' own. */
+int gqa_prefill_sliding_window(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                               const int32_t* seq_lens, void* o, int32_t B, int32_t N,
+                               int32_t S_max, int32_t window, int32_t dtype, void* stream);
+int gqa_prefill_sliding_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages,
+                                     const int32_t* cu_q, const int32_t* seq_lens, void* o,
+                                     int32_t B, int32_t N, int32_t num_pages, int32_t window,
+                                     int32_t dtype, void* stream);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:

@@ -234,6 +234,14 @@ def test_prefill_arguments_fail_before_launch(lib):
     assert fp(ok, ok, ok, None, 8, ok, ok, ok, 2, 64, 8, 1, None) == -1
     assert fp(ok, ok, ok, ok, 0, ok, ok, ok, 2, 64, 8, 1, None) == -2
     assert fp(ok, ok, ok, ok, 8, ok, ok, ok, 2, 64, 0, 1, None) == -2
+    # runtime-window prefill: fw(q, k, v, cu_q, seq_lens, o, B, N, S_max, window, dtype, s)
+    fw, fwp = lib.gqa_prefill_sliding_window, lib.gqa_prefill_sliding_window_paged
+    for w in (0, -1, 262145):
+        assert fw(ok, ok, ok, ok, ok, ok, 2, 64, 128, w, 1, None) == -2
+        # fwp(q, k_pool, v_pool, bt, max_pages, cu_q, seq_lens, o, B, N, num_pages, window, dt, s)
+        assert fwp(ok, ok, ok, ok, 8, ok, ok, ok, 2, 64, 8, w, 1, None) == -2
+    assert fw(ok, ok, ok, None, ok, ok, 2, 64, 128, 2048, 1, None) == -1
+    assert fw(ok, ok, ok, ok, ok, ok, 2, 64, 128, 2048, 3, None) == -3
 
 
 def test_binding_refuses_host_tensors(lib):

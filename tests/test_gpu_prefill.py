@@ -162,3 +162,44 @@ def test_prefill_chunk_longer_than_sequence():
     ref = oracle_prefill(c)
     assert not got[:3].any()           # tokens 0..2 of sequence 0 sit before position 0
     assert max_err(got, ref) <= TOL["bf16"]
+
+
+# Runtime windows of the sliding geometry (the Retrofit page's per-layer
+# windows): chunks after pasts around the window edge, a single token, a fresh
+# prompt and an empty chunk.
+@pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("window", [1, 17, 2048, 8192])
+def test_prefill_window_parity(window, dtype, paged):
+    cap = max(window + 64, 608)
+    lens = [cap - 3, min(cap, window + 20), min(cap, window), 40, 7]
+    q_lens = [60, 25, 1, 40, 0]
+    c = synth.make_prefill_case("sliding", dtype, cap, lens, q_lens, paged=paged, seed=510 + window,
+                                window=window, extra_pages=3)
+    d = to_gpu(c)
+    got = to_f64(gqa.gqa_prefill_sliding_window(d.q, d.k, d.v, d.cu_q, d.seq_lens, window,
+                                                block_table=d.block_table))
+    assert np.isfinite(got).all()  # NaN outside every attended range is never read
+    err = max_err(got, oracle_prefill(c))
+    assert err <= TOL[dtype], (window, dtype, paged, err)
+
+
+def test_prefill_window_1024_matches_the_default_entry_point():
+    c = to_gpu(synth.make_prefill_case("sliding", "bf16", 2112, [1300, 40, 2100], [77, 40, 300],
+                                       seed=511))
+    a = hip_prefill(c)
+    b = gqa.gqa_prefill_sliding_window(c.q, c.k, c.v, c.cu_q, c.seq_lens, 1024)
+    assert torch.equal(a, b)
+
+
+def test_prefill_window_8192_sampled():
+    # 2 x 1024 new tokens after 8192 cached positions, window 8192: sampled rows
+    W = 8192
+    c = synth.make_prefill_case("sliding", "bf16", 9232, [9216, 9000], [1024, 1024], seed=512,
+                                window=W, device="cuda", fill=0.0)
+    got = to_f64(gqa.gqa_prefill_sliding_window(c.q, c.k, c.v, c.cu_q, c.seq_lens, W))
+    assert np.isfinite(got).all()
+    rows = [(n, h) for n in (0, 511, 1023, 1024, 2047) for h in (0, 17, 31)]
+    ref = oracle_prefill(to_cpu(c), rows=rows)
+    for i, (n, h) in enumerate(rows):
+        assert max_err(got[n, h], ref[i]) <= TOL["bf16"], (n, h)
