@@ -176,14 +176,25 @@ def bench_prefill(seed, dev, stream) -> dict:
 
     log("prefill / chunked prefill (MFMA-bound; algorithmic flops of the unmasked pairs)")
     pre = {}
-    for name in sorted(synth.PREFILL_WORKLOADS):
-        pc = synth.make_prefill_workload(name, seed=seed, device=dev, fill=0.0)
-        fn = gqa.gqa_prefill_sliding if pc.variant == "sliding" else gqa.gqa_prefill_global
+    # the two workloads, then the sliding one at the Retrofit page's wider
+    # per-layer windows (runtime-window entry point)
+    runs = [(name, None) for name in sorted(synth.PREFILL_WORKLOADS)]
+    runs += [("sliding_bf16_prefill_b8_past4096_chunk2048", w) for w in (2048, 4096)]
+    for name, window in runs:
+        pc = synth.make_prefill_workload(name, seed=seed, device=dev, fill=0.0, window=window)
         o_pf = torch.empty_like(pc.q)
+        if window is not None:
+            name = f"{name}_window{window}"
 
-        def pf_call():
-            fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
-               stream=stream)
+            def pf_call():
+                gqa.gqa_prefill_sliding_window(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, window,
+                                               block_table=pc.block_table, o=o_pf, stream=stream)
+        else:
+            fn = gqa.gqa_prefill_sliding if pc.variant == "sliding" else gqa.gqa_prefill_global
+
+            def pf_call():
+                fn(pc.q, pc.k, pc.v, pc.cu_q, pc.seq_lens, block_table=pc.block_table, o=o_pf,
+                   stream=stream)
 
         for _ in range(SECTION_WARMUP):
             pf_call()

@@ -348,12 +348,13 @@ PREFILL_WORKLOADS = {
 
 
 def make_prefill_workload(name: str, seed: int = 0, device="cpu",
-                          fill: float = float("nan")) -> PrefillCase:
+                          fill: float = float("nan"), window: int | None = None) -> PrefillCase:
+    """One of PREFILL_WORKLOADS by name; `window` overrides the sliding window."""
     w = PREFILL_WORKLOADS[name]
     L = w["past"] + w["chunk"]
     cap = (L + PAGE - 1) // PAGE * PAGE
     return make_prefill_case(w["variant"], w["dtype"], cap, [L] * w["B"], [w["chunk"]] * w["B"],
-                             paged=w["paged"], seed=seed, device=device, fill=fill)
+                             paged=w["paged"], seed=seed, device=device, fill=fill, window=window)
 
 
 def make_workload(name: str, seed: int = 0, device="cpu", fill: float = float("nan"),
