@@ -225,7 +225,22 @@ def _dev(t: torch.Tensor, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _prepare(variant, q, seq_lens, o, workspace, capacity, window=None):
+def _for_stream(t: torch.Tensor, stream) -> torch.Tensor:
+    """A tensor this binding allocated, used by a launch on `stream`.
+
+    torch's caching allocator ties a block to the stream that was current when
+    it was allocated and may hand it out again as soon as the tensor is freed,
+    ordered only against that stream.  When the launch runs on another stream,
+    record_stream makes the free wait for the work queued on `stream` up to
+    the moment of the free, so the caller keeps the tensor alive until the
+    launch has been queued (the workspace is then freed when the call
+    returns)."""
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
+def _prepare(variant, q, seq_lens, o, workspace, capacity, window=None, stream=None):
     B = q.shape[0]
     D = 256 if variant == GQA_SLIDING else 512
     if q.dim() != 3 or q.shape[1:] != (HEADS, D):
@@ -233,15 +248,17 @@ def _prepare(variant, q, seq_lens, o, workspace, capacity, window=None):
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
     if o is None:
-        o = torch.empty_like(q)
+        o = _for_stream(torch.empty_like(q), stream)
     elif o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
     need = gqa_decode_workspace_bytes(variant, B, capacity, window)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _for_stream(torch.empty(need, dtype=torch.uint8, device=q.device), stream)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return B, o, ws_ptr, ws_bytes
+    # the workspace tensor goes back to the caller, which holds it across the
+    # launch (see _for_stream)
+    return B, o, (workspace, ws_ptr), ws_bytes
 
 
 def _stream(stream, device):
@@ -257,11 +274,12 @@ def _contiguous_call(name, variant, q, k, v, seq_lens, o, workspace, stream, win
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     S_max = k.shape[1]
-    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, S_max, window)
+    B, o, (ws_keep, ws), ws_bytes = _prepare(variant, q, seq_lens, o, workspace, S_max, window, stream)
     fn = getattr(library(), name)
     shape = (B, S_max) if window is None else (B, S_max, int(window))
     rc = fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
             *shape, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    del ws_keep  # held until the launch was queued (see _for_stream)
     if rc:
         raise GqaError(name, rc)
     return o
@@ -280,12 +298,14 @@ def _paged_call(name, variant, q, k_pool, v_pool, block_table, seq_lens, o, work
         raise ValueError("block_table must be int32 [B,max_pages]")
     max_pages = block_table.shape[1]
     num_pages = k_pool.shape[0]
-    B, o, ws, ws_bytes = _prepare(variant, q, seq_lens, o, workspace, max_pages * PAGE, window)
+    B, o, (ws_keep, ws), ws_bytes = _prepare(variant, q, seq_lens, o, workspace, max_pages * PAGE, window,
+                                  stream)
     fn = getattr(library(), name)
     shape = (B, num_pages) if window is None else (B, num_pages, int(window))
     rc = fn(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
             _dev(block_table, "block_table"), max_pages, _dev(seq_lens, "seq_lens"), _dev(o, "o"),
             *shape, _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    del ws_keep  # held until the launch was queued (see _for_stream)
     if rc:
         raise GqaError(name, rc)
     return o
@@ -350,7 +370,7 @@ def _append_call(variant, q_raw, k_raw, v_raw, w_q, w_k, seq_lens, k_cache, v_ca
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
     if q_out is None:
-        q_out = torch.empty_like(q_raw)
+        q_out = _for_stream(torch.empty_like(q_raw), stream)
     lib = library()
     st = _stream(stream, q_raw.device)
     ptrs = [_dev(q_raw, "q_raw"), _dev(k_raw, "k_raw")]
@@ -404,12 +424,13 @@ def gqa_decode_sliding_ring(q, k, v, seq_lens, window: int = 1024, o=None, works
     B = q.shape[0]
     need = gqa_decode_sliding_ring_workspace_bytes(B, ring, window)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    B, o, ws, ws_bytes = _prepare(GQA_SLIDING, q, seq_lens, o, workspace, ring, window)
+        workspace = _for_stream(torch.empty(need, dtype=torch.uint8, device=q.device), stream)
+    B, o, (ws_keep, ws), ws_bytes = _prepare(GQA_SLIDING, q, seq_lens, o, workspace, ring, window, stream)
     rc = library().gqa_decode_sliding_ring(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                            _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, ring,
                                            int(window), _dtype_code(q), ws, ws_bytes,
                                            _stream(stream, q.device))
+    del ws_keep  # held until the launch was queued (see _for_stream)
     if rc:
         raise GqaError("gqa_decode_sliding_ring", rc)
     return o
@@ -453,11 +474,12 @@ def gqa_decode_global_k_eq_v(q, v, w_k, seq_lens, o=None, workspace=None, stream
         raise TypeError("q and v must share a dtype")
     _check_w_k(w_k, q)
     S_max = v.shape[1]
-    B, o, ws, ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, S_max)
+    B, o, (ws_keep, ws), ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, S_max, stream=stream)
     name = "gqa_decode_global_k_eq_v"
     rc = getattr(library(), name)(_dev(q, "q"), _dev(v, "v"), _dev(w_k, "w_k"),
                                   _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, S_max,
                                   _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    del ws_keep  # held until the launch was queued (see _for_stream)
     if rc:
         raise GqaError(name, rc)
     return o
@@ -475,12 +497,14 @@ def gqa_decode_global_k_eq_v_paged(q, v_pool, w_k, block_table, seq_lens, o=None
             block_table.shape[0] != q.shape[0]:
         raise ValueError("block_table must be int32 [B,max_pages]")
     max_pages = block_table.shape[1]
-    B, o, ws, ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, max_pages * PAGE)
+    B, o, (ws_keep, ws), ws_bytes = _prepare(GQA_GLOBAL, q, seq_lens, o, workspace, max_pages * PAGE,
+                                  stream=stream)
     name = "gqa_decode_global_k_eq_v_paged"
     rc = getattr(library(), name)(_dev(q, "q"), _dev(v_pool, "v_pool"), _dev(w_k, "w_k"),
                                   _dev(block_table, "block_table"), max_pages,
                                   _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, v_pool.shape[0],
                                   _dtype_code(q), ws, ws_bytes, _stream(stream, q.device))
+    del ws_keep  # held until the launch was queued (see _for_stream)
     if rc:
         raise GqaError(name, rc)
     return o
@@ -500,7 +524,7 @@ def gqa_append_global_k_eq_v(q_raw, k_raw, w_q, w_k, seq_lens, v_cache, block_ta
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
     if q_out is None:
-        q_out = torch.empty_like(q_raw)
+        q_out = _for_stream(torch.empty_like(q_raw), stream)
     lib = library()
     st = _stream(stream, q_raw.device)
     ptrs = [_dev(q_raw, "q_raw"), _dev(k_raw, "k_raw"), _dev(w_q, "w_q"), _dev(w_k, "w_k")]
@@ -539,7 +563,7 @@ def _prefill_call(variant, q, k, v, cu_q, seq_lens, block_table, o, stream, wind
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     if o is None:
-        o = torch.empty_like(q)
+        o = _for_stream(torch.empty_like(q), stream)
     elif o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
     N = q.shape[0]

@@ -50,6 +50,17 @@ struct Elem<false> {
   static constexpr int bytes = 4;
 };
 
+// Sixteen positions of zeros in the widest row layout of any variant
+// (16 kv heads x 256 f32, the same bytes as 4 x 512 f32): the rows a kernel
+// reads in place of a page whose id lies outside the pool, so that such a page
+// is never dereferenced and no other cache memory stands in for it.  Device
+// code only reads it; a __device__ array without initializer is zero-filled
+// when the code object is loaded.
+constexpr size_t kZeroPageBytes = (size_t)kPage * 16 * 256 * 4;
+__device__ __attribute__((aligned(256))) u32x4 g_zero_page[kZeroPageBytes / 16];
+
+__device__ inline const char* zero_page() { return reinterpret_cast<const char*>(g_zero_page); }
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -274,7 +274,14 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       const int page = i < 64 ? __builtin_amdgcn_readlane(pg_cur, i)
                               : __builtin_amdgcn_readlane(pg_nxt, i - 64);
       ta.ok = page >= 0 && page < a.num_pages;
-      off = ((size_t)(ta.ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+      if (!ta.ok) {
+        // a page id outside the pool is never dereferenced: its rows come
+        // from the library's zero page (a scalar select) and its logits are
+        // set to -inf below, so its positions drop out of the softmax
+        ta.kb = ta.vb = zero_page() + (size_t)g * ROW;
+        return ta;
+      }
+      off = ((size_t)page * kPage * KV + g) * (size_t)ROW;
     } else {
       ta.ok = true;
       // a ring of a multiple of 16 slots never splits a 16-aligned tile

@@ -250,7 +250,11 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
                   "register staging: a thread's rows stay within one 16-row half");
     auto fetch = [&](int step, int& okbits, auto& dst) {
       const int pos0 = step * PT;
-      size_t base[NH];
+      // K and V rows of the step's 16-row halves (wave-uniform pointers); a
+      // page id outside the pool is never dereferenced: its half reads the
+      // library's zero page and its keys are masked in compute()
+      const char* kh[NH];
+      const char* vh[NH];
       okbits = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
@@ -264,10 +268,14 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int page = __builtin_amdgcn_readlane(bt_lane, pi & 63);
           const bool ok = page >= 0 && page < a.num_pages;
           okbits |= ok ? (1 << h) : 0;
-          base[h] = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
+          const size_t off = ((size_t)page * kPage * KV + g) * (size_t)ROW;
+          kh[h] = ok ? a.k + off : zero_page() + (size_t)g * ROW;
+          vh[h] = ok ? a.v + off : zero_page() + (size_t)g * ROW;
         } else {
           okbits |= 1 << h;
-          base[h] = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
+          const size_t off = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
+          kh[h] = a.k + off;
+          vh[h] = a.v + off;
         }
       }
       if constexpr (DMA) {
@@ -279,8 +287,8 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
         // operand reads of the step being computed.)
         auto dma = [&](int which, int h, int row_in_half, int part, int lds_off) {
           // the descriptor's base is wave-uniform: keep it in scalar registers
-          const uint64_t addr =
-              (uint64_t)((which ? a.v : a.k) + (NH == 1 || h == 0 ? base[0] : base[NH - 1]));
+          const int hh = NH == 1 || h == 0 ? 0 : NH - 1;
+          const uint64_t addr = (uint64_t)(which ? vh[hh] : kh[hh]);
           const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
           const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
           const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -320,8 +328,9 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int which = (RPU * u) / PT;               // 0: K, 1: V
           const int rin = (RPU * u) % PT;                 // + row0 < 16 within its half
           const int h = rin / 16;
-          const size_t off = base[NH == 1 ? 0 : h] + (size_t)(ld_row0 + rin % 16) * POS + ld_c * 16;
-          ld[u] = load16((which ? a.v : a.k) + off);
+          const int hh = NH == 1 ? 0 : h;
+          const size_t off = (size_t)(ld_row0 + rin % 16) * POS + ld_c * 16;
+          ld[u] = load16((which ? vh[hh] : kh[hh]) + off);
         }
       } else {
 #pragma unroll
@@ -332,9 +341,9 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int c = q % NCH;
           const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
           const int h = rel >> 4;
-          size_t off = (NH == 1 ? base[0] : (h ? base[NH - 1] : base[0])) +
-                       (size_t)(rel & 15) * POS + c * 16;
-          ld[u] = load16((which ? a.v : a.k) + off);
+          const int hh = NH == 1 ? 0 : (h ? NH - 1 : 0);
+          const size_t off = (size_t)(rel & 15) * POS + c * 16;
+          ld[u] = load16((which ? vh[hh] : kh[hh]) + off);
         }
       }
     };

@@ -221,6 +221,8 @@ def test_deterministic_and_workspace_reuse(variant):
     need = gqa.gqa_decode_workspace_bytes(variant, 4, cap)
     ws = torch.full((max(need, 16),), 255, dtype=torch.uint8, device="cuda")  # NaN-patterned
     s = torch.cuda.Stream()
+    # the inputs and the NaN fill were queued on the current stream
+    s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         o1 = hip_run(a, workspace=ws, stream=s)
         ob = hip_run(b, workspace=ws, stream=s)
@@ -228,6 +230,34 @@ def test_deterministic_and_workspace_reuse(variant):
     s.synchronize()
     assert torch.equal(o1, o2)
     assert max_err(to_f64(ob), oracle_run(b)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_side_stream_without_entering_it(variant):
+    # stream= names a side stream while the current stream stays the default
+    # one; the binding allocates o and the workspace itself.  Work queued on
+    # the default stream right after the call allocates and fills memory of
+    # the workspace's size: the binding must keep the blocks it handed to the
+    # side stream's kernels from being reused before they complete.
+    cap = 4096
+    c = to_gpu(synth.make_case(variant, "bf16", 4, cap, [4096, 5, 3000, 1], seed=115))
+    assert gqa.gqa_decode_plan(variant, 4, cap)["mode"] == "stream"
+    need = gqa.gqa_decode_workspace_bytes(variant, 4, cap)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        o = hip_run(c, stream=s)
+        junk = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+        junk2 = torch.full_like(o, float("nan"))
+        outs.append(o)
+        del junk, junk2
+    s.synchronize()
+    torch.cuda.synchronize()
+    ref = oracle_run(c)
+    for o in outs:
+        assert max_err(to_f64(o), ref) <= TOL["bf16"]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
 def test_profile_hooks_count_launches():
@@ -323,69 +353,9 @@ def test_window_poison_never_read():
 
 # --------------------------------------------------------------- full-size workloads
 
-def _sample_rows(case, n_seq, seed):
-    g = torch.Generator().manual_seed(seed)
-    bs = torch.randperm(case.B, generator=g)[:n_seq].tolist()
-    return [(b, h) for b in bs for h in range(HEADS)]
-
-
 @pytest.mark.parametrize("name", ["sliding_f32_b4_s2048", "global_bf16_b4_s4096"])
 def test_workload_small_full_parity(name):
     c = synth.make_workload(name, seed=0)
     got = to_f64(hip_run(to_gpu(c)))
     err = max_err(got, oracle_run(c))
     assert err <= TOL[c.dtype], (name, err)
-
-
-def test_workload_sliding_b256_sampled():
-    name = "sliding_bf16_b256_s8192"
-    c = synth.make_workload(name, seed=0, device="cuda")
-    got = hip_run(c)
-    torch.cuda.synchronize()
-    assert torch.isfinite(got.float()).all()
-    lens = c.seq_lens.cpu()
-    # sampled sequences, incl. the shortest and the longest: the oracle on their slice
-    order = torch.argsort(lens)
-    pick = sorted(set([int(order[0]), int(order[-1])] +
-                      torch.randperm(c.B, generator=torch.Generator().manual_seed(5))[:6].tolist()))
-    for b in pick:
-        sub = synth.Case(c.variant, c.dtype, c.q[b:b + 1].cpu(), c.k[b:b + 1].cpu(),
-                         c.v[b:b + 1].cpu(), lens[b:b + 1], None, c.cap, c.window)
-        err = max_err(to_f64(got[b:b + 1]), oracle_run(sub))
-        assert err <= TOL["bf16"], (b, int(lens[b]), err)
-
-
-def test_workload_global_b32_paged_sampled():
-    name = "global_bf16_b32_paged_s16k_128k"
-    c = synth.make_workload(name, seed=0, device="cuda")
-    got = hip_run(c)
-    torch.cuda.synchronize()
-    assert torch.isfinite(got.float()).all()
-    host = synth.Case(c.variant, c.dtype, c.q.cpu(), c.k.cpu(), c.v.cpu(), c.seq_lens.cpu(),
-                      c.block_table.cpu(), c.cap, c.window)
-    lens = host.seq_lens
-    order = torch.argsort(lens)
-    bs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    rows = [(b, h) for b in bs for h in (0, 7, 8, 31)]
-    ref = oracle_run(host, rows=rows)
-    gh = to_f64(got)
-    for i, (b, h) in enumerate(rows):
-        err = max_err(gh[b, h], ref[i])
-        assert err <= TOL["bf16"], (b, h, int(lens[b]), err)
-
-
-@pytest.mark.parametrize("name", ["sliding_bf16_b1_paged_s262144",
-                                  "global_bf16_b1_paged_s262144"])
-def test_workload_long_single_sequence(name):
-    c = synth.make_workload(name, seed=0, device="cuda")
-    got = hip_run(c)
-    torch.cuda.synchronize()
-    host = synth.Case(c.variant, c.dtype, c.q.cpu(), c.k.cpu(), c.v.cpu(), c.seq_lens.cpu(),
-                      c.block_table.cpu(), c.cap, c.window)
-    heads = range(HEADS) if c.variant == "sliding" else (0, 9, 22, 31)
-    rows = [(0, h) for h in heads]
-    ref = oracle_run(host, rows=rows)
-    gh = to_f64(got)
-    for i, (b, h) in enumerate(rows):
-        err = max_err(gh[b, h], ref[i])
-        assert err <= TOL["bf16"], (h, err)
