@@ -50,6 +50,7 @@ from ._lib import (  # noqa: F401
     gqa_decode_global_k_eq_v,
     gqa_decode_global_k_eq_v_paged,
     gqa_decode_global_paged,
+    gqa_decode_global_paged_noalloc,
     gqa_decode_plan,
     gqa_decode_sliding,
     gqa_decode_sliding_paged,

@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "gqa_prefill_sliding_paged", "gqa_prefill_global_paged", "gqa_decode_sliding_ring",
     "gqa_decode_sliding_ring_workspace_bytes", "gqa_append_sliding_ring",
     "gqa_prefill_sliding_window", "gqa_prefill_sliding_window_paged",
+    "gqa_decode_global_paged_noalloc",
 )
 
 
@@ -55,6 +56,8 @@ def library():
                        ("gqa_decode_sliding_paged", paged), ("gqa_decode_global_paged", paged)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lib.gqa_decode_global_paged_noalloc.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, p]
+    lib.gqa_decode_global_paged_noalloc.restype = ctypes.c_int
     lib.gqa_decode_sliding_window.argtypes = [p, p, p, p, p, i32, i32, i32, i32, p, sz, p]
     lib.gqa_decode_sliding_window.restype = ctypes.c_int
     lib.gqa_decode_sliding_window_paged.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, i32, p,
@@ -335,6 +338,34 @@ def gqa_decode_global_paged(q, k_pool, v_pool, block_table, seq_lens, o=None, wo
     """decodeGQA on a paged cache k_pool, v_pool [num_pages,16,4,512]."""
     return _paged_call("gqa_decode_global_paged", GQA_GLOBAL, q, k_pool, v_pool, block_table,
                        seq_lens, o, workspace, stream)
+
+
+def gqa_decode_global_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, o, stream=None):
+    """decodeGQA on a paged cache through the entry point that allocates
+    nothing: its split-S partials use the library's own device array (shared
+    by every call on the device; calls that can overlap must be ordered by the
+    caller).  `o` is required: this call allocates no tensor either."""
+    if not isinstance(o, torch.Tensor) or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must be given and match q in shape and dtype")
+    if q.dim() != 3 or q.shape[1:] != (HEADS, 512):
+        raise ValueError("q must be [B,32,512]")
+    if k_pool.dim() != 4 or k_pool.shape[1:] != (PAGE, 4, 512) or v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool/v_pool must be [num_pages,16,4,512]")
+    if not (q.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("q, k_pool, v_pool must share a dtype")
+    B = q.shape[0]
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B,max_pages]")
+    name = "gqa_decode_global_paged_noalloc"
+    rc = getattr(library(), name)(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                  _dev(block_table, "block_table"), block_table.shape[1],
+                                  _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, k_pool.shape[0],
+                                  _dtype_code(q), _stream(stream, q.device))
+    if rc:
+        raise GqaError(name, rc)
+    return o
 
 
 def gqa_decode_sliding_window(q, k, v, seq_lens, window, o=None, workspace=None, stream=None):

@@ -36,6 +36,7 @@
 // the same tile and dropped through -inf logits, so NaN or stale data in
 // unused cache space cannot reach the result).
 
+#include <mutex>
 #include <vector>
 
 #include "gqa_common.h"
@@ -1298,6 +1299,47 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   return GQA_OK;
 }
 
+// ---- the workspace of the allocation-free entry point
+// gqa_decode_global_paged_noalloc runs with this file-scope array as its
+// workspace, for callers that cannot allocate device memory.  Its size is the
+// workspace of the largest batch the global geometry accepts (B = 256 in
+// stream mode: 1,280 + 131,072 + 33,554,432 bytes), rounded up to 33 MiB.
+// Each device that loads the library holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), looked up with that device current on the first call
+// and kept; nullptr on a HIP error.
+void* scratch_address(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // ---- launch timing (measurement only)
 struct ProfRec {
   int kind;
@@ -1359,7 +1401,8 @@ constexpr int kProfKeysFromValues = 6;
 int run(int variant, int window, bool paged, const void* q, const void* k, const void* v,
         const void* w_k, const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
         void* o, int32_t B, int32_t S_max, int32_t num_pages, int32_t dtype, void* workspace,
-        size_t workspace_bytes_given, void* stream_, int32_t ring = 0) {
+        size_t workspace_bytes_given, void* stream_, int32_t ring = 0,
+        bool workspace_from_scratch = false) {
   const bool kfv = w_k != nullptr;
   if (kfv && variant != GQA_GLOBAL) return GQA_ERR_DTYPE;
   if (!q || (!k && !kfv) || !v || !seq_lens || !o || (paged && !block_table)) return GQA_ERR_NULL;
@@ -1387,6 +1430,13 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   if (rc) return rc;
   const bool unit_mode = plan.mode == GQA_MODE_UNIT;
   if (!unit_mode) {
+    if (workspace_from_scratch) {
+      // every host check above has passed: only now is HIP asked for the array
+      if (plan.total > kScratchBytes) return GQA_ERR_WORKSPACE;
+      workspace = scratch_address(reinterpret_cast<hipStream_t>(stream_));
+      if (workspace == nullptr) return GQA_ERR_HIP;
+      workspace_bytes_given = kScratchBytes;
+    }
     if (!workspace || workspace_bytes_given < plan.total) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_ALIGN;
   }
@@ -1559,6 +1609,14 @@ int gqa_decode_global_paged(const void* q, const void* k_pool, const void* v_poo
                             void* stream) {
   return run(GQA_GLOBAL, 0, true, q, k_pool, v_pool, nullptr, block_table, max_pages, seq_lens, o, B, 0,
              num_pages, dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_global_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, void* o, int32_t B,
+                                    int32_t num_pages, int32_t dtype, void* stream) {
+  return run(GQA_GLOBAL, 0, true, q, k_pool, v_pool, nullptr, block_table, max_pages, seq_lens, o,
+             B, 0, num_pages, dtype, nullptr, 0, stream, 0, true);
 }
 
 int gqa_decode_sliding_window(const void* q, const void* k, const void* v,

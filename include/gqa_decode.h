@@ -288,6 +288,26 @@ int gqa_prefill_sliding_window_paged(const void* q, const void* k_pool, const vo
                                      int32_t B, int32_t N, int32_t num_pages, int32_t window,
                                      int32_t dtype, void* stream);
 
+/* decodeGQA on a paged cache without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, layouts, results and
+ * errors are those of gqa_decode_global_paged with workspace and
+ * workspace_bytes left out: the split-S partials go to a library-owned array
+ * of GQA_NOALLOC_SCRATCH_BYTES bytes in device memory (the workspace of the
+ * largest batch, B = 256), which each device that loads the library holds
+ * until the process ends.  The call itself allocates nothing; a plan needing
+ * more than that array returns GQA_ERR_WORKSPACE.  The first call on a device
+ * looks up the array's address with that device current (HIP may load the
+ * library's code object then), so make it outside graph capture.  All calls
+ * on one device share the one array and every call overwrites it: calls that
+ * can overlap on a device (other streams, other threads) race and must be
+ * ordered by the caller.  Nothing in the array needs to start at zero. */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)33 << 20)
+int gqa_decode_global_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, void* o, int32_t B,
+                                    int32_t num_pages, int32_t dtype, void* stream);
+
 /* Workspace bytes a call needs for `variant` (GQA_SLIDING / GQA_GLOBAL), batch B
  * and cache capacity (S_max, or max_pages*16 for the paged forms).  Depends on
  * nothing else (not on dtype, device or seq_lens).  0 means no split-S pass:
