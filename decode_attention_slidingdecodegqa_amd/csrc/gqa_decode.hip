@@ -91,6 +91,19 @@ __device__ inline int wave_of(long t, long T, int W) {
   return (int)(((t + 1) * W - 1) / T);
 }
 
+// Waves that share the T tiles of a stream-mode call: the W launched, or
+// only max(T, kMinStreamWaves) of them when the actual lengths give fewer
+// tiles than waves (the rest leave at once and hold no slice, so the combine
+// reads no empty slots).  Folding several tiles into each wave to save
+// partials measured slower: a global call of 4 sequences over 4096 positions
+// took 30.8 us in its main kernel at 256 waves of about 6 tiles, 21 us at
+// 1024 waves of 1.6.  The main and combine kernels both derive it from T.
+constexpr int kMinStreamWaves = 256;
+__device__ inline int effective_waves(long T, int W) {
+  const long w = T > kMinStreamWaves ? T : kMinStreamWaves;
+  return w < W ? (int)w : W;
+}
+
 // Waves per SIMD the main kernels are compiled for: the sliding bf16 kernels
 // fit two (<= 256 registers), the others need one.
 template <int KV, bool BF16>
@@ -671,8 +684,10 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   const long T = (long)KV * s_before[a.B];  // tiles of all units
 
   // ---- this wave's slice [s_begin, s_end) of the flattened tiles
-  const long s_begin = (long)w * T / a.n_waves;
-  const long s_end = (long)(w + 1) * T / a.n_waves;
+  const int W = effective_waves(T, a.n_waves);
+  if (w >= W) return;
+  const long s_begin = (long)w * T / W;
+  const long s_end = (long)(w + 1) * T / W;
   if (s_begin >= s_end) return;
 
   // the sequence holding s_begin: the last one whose first tile is <= s_begin
@@ -833,17 +848,21 @@ struct CombineArgs {
   int32_t n_waves;
 };
 
-// One work-group of kCombineWaves waves per (sequence, query head, d part):
+// One work-group of CW waves (8, or 4 when that many work-groups would not
+// fit the part in one round) per (sequence, query head, d part):
 // the head's D values are cut into DS parts of D/DS (DS > 1 when there are
 // few sequences, so that more work-groups share the reads).  Wave w merges the
-// partials w, w + kCombineWaves, ... of the unit: lane l owns PER = D/(64 DS)
+// partials w, w + CW, ... of the unit: lane l owns PER = D/(64 DS)
 // consecutive d values of the part, with U partials in flight (more for
 // narrower lanes).  The waves' sums are then added in LDS in wave order.  The
 // first batch of partial rows is loaded together with the (m, l) pairs the
 // reference max needs, since those loads do not depend on it.  A unit held by
 // one slice was written by its wave; a sequence with nothing attended gets a
 // zero row.
-constexpr int kCombineWaves = 8;
+constexpr int kCombineWavesMax = 8;
+// work-groups of eight waves one combine launch may hold before it takes
+// four-wave groups: about one round over 256 CUs at the kernel's occupancy
+constexpr int kCombineWideGroups = 512;
 
 // PER consecutive floats at p (16-, 8- or 4-byte aligned as PER asks)
 template <int PER>
@@ -865,8 +884,8 @@ __device__ __forceinline__ void load_floats(const float* p, float (&v)[PER]) {
   }
 }
 
-template <int KV, int D, bool BF16, int DS>
-__global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(CombineArgs a) {
+template <int KV, int D, bool BF16, int DS, int CW>
+__global__ __launch_bounds__(64 * CW) void gqa_combine_kernel(CombineArgs a) {
   constexpr int G = kHeads / KV;
   constexpr int EB = Elem<BF16>::bytes;
   constexpr int DW = D / DS;   // d values of this work-group
@@ -875,8 +894,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
   // partials in flight per lane: a batch is one round trip, so narrow lanes
   // take more of them (about 64 registers of partial rows either way)
   constexpr int U = PER >= 4 ? 8 : 16;
-  __shared__ __attribute__((aligned(16))) float s_acc[kCombineWaves][DW];
-  __shared__ float s_l[kCombineWaves];
+  __shared__ __attribute__((aligned(16))) float s_acc[CW][DW];
+  __shared__ float s_l[CW];
   const int bh = blockIdx.x / DS;
   const int part = blockIdx.x % DS;
   const int b = bh / kHeads;
@@ -918,8 +937,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
     return;
   }
   const long s0 = P0 + (long)g * n;
-  const int wf = wave_of(s0, T, a.n_waves);
-  const int wl = wave_of(s0 + n - 1, T, a.n_waves);
+  const int W = effective_waves(T, a.n_waves);
+  const int wf = wave_of(s0, T, W);
+  const int wl = wave_of(s0 + n - 1, T, W);
   if (wf == wl) return;  // written by the wave that held the whole unit
   const int ns = wl - wf + 1;
   const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + ((size_t)unit + wf) * G + hh;
@@ -931,8 +951,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
   // tested with double divisions, exact here: (w+1)T < 2^53 is exact, the
   // quotient is correctly rounded, and a quotient that is not an integer lies
   // at least 1/W from one
-  const bool all_hold = T >= a.n_waves;
-  const double Td = (double)T, Wd = (double)a.n_waves;
+  const bool all_hold = T >= W;
+  const double Td = (double)T, Wd = (double)W;
   auto holds = [&](int s) {
     if (all_hold) return true;
     const double w = (double)(wf + s);
@@ -945,7 +965,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
   auto load_batch = [&](int s0u) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int su = s0u + kCombineWaves * u;
+      const int su = s0u + CW * u;
       const int s = su < ns ? su : ns - 1;
       e[u] = ml[(size_t)s * G];
       okb[u] = su < ns && holds(s);
@@ -980,7 +1000,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
     }
   };
   accumulate();
-  for (int s0u = wave + kCombineWaves * U; s0u < ns; s0u += kCombineWaves * U) {
+  for (int s0u = wave + CW * U; s0u < ns; s0u += CW * U) {
     load_batch(s0u);
     accumulate();
   }
@@ -994,7 +1014,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
 #pragma unroll
   for (int i = 0; i < PER; ++i) run[i] = 0.f;
 #pragma unroll
-  for (int w = 0; w < kCombineWaves; ++w) {
+  for (int w = 0; w < CW; ++w) {
     L += s_l[w];
 #pragma unroll
     for (int i = 0; i < PER; ++i) run[i] += s_acc[w][dl + i];
@@ -1006,11 +1026,14 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gqa_combine_kernel(Combine
 }
 
 // d parts per (sequence, head) of the combine: enough work-groups to spread
-// the partial reads (at least 1024 when D allows it; one lane per d at most)
+// the partial reads over the CUs (at least 256 when D allows it; one lane
+// per d at most).  With 1024 groups of one float per lane, a global call of 4
+// sequences spent 12.8 us in its combine, more than one sequence's 256
+// groups merging four times the slices (8.6 us).
 template <int D>
 inline int combine_parts(int B) {
   int ds = 1;
-  while (ds < D / 64 && (long)B * kHeads * ds < 1024) ds *= 2;
+  while (ds < D / 64 && (long)B * kHeads * ds < 256) ds *= 2;
   return ds;
 }
 
@@ -1372,20 +1395,31 @@ MainFn pick_main(bool unit_mode, bool paged, bool bf16) {
 }
 
 template <int KV, int D, int DS>
-CombineFn pick_combine_ds(bool bf16) {
-  return bf16 ? gqa_combine_kernel<KV, D, true, DS> : gqa_combine_kernel<KV, D, false, DS>;
+CombineFn pick_combine_ds(bool bf16, int cw) {
+  if (cw == kCombineWavesMax)
+    return bf16 ? gqa_combine_kernel<KV, D, true, DS, kCombineWavesMax>
+                : gqa_combine_kernel<KV, D, false, DS, kCombineWavesMax>;
+  return bf16 ? gqa_combine_kernel<KV, D, true, DS, kCombineWavesMax / 2>
+              : gqa_combine_kernel<KV, D, false, DS, kCombineWavesMax / 2>;
 }
 
 template <int KV, int D>
-CombineFn pick_combine(bool bf16, int ds) {
+CombineFn pick_combine(bool bf16, int ds, int cw) {
   switch (ds) {
-    case 1: return pick_combine_ds<KV, D, 1>(bf16);
-    case 2: return pick_combine_ds<KV, D, 2>(bf16);
-    case 4: return pick_combine_ds<KV, D, 4>(bf16);
+    case 1: return pick_combine_ds<KV, D, 1>(bf16, cw);
+    case 2: return pick_combine_ds<KV, D, 2>(bf16, cw);
+    case 4: return pick_combine_ds<KV, D, 4>(bf16, cw);
     default:
-      if constexpr (D / 64 >= 8) return pick_combine_ds<KV, D, 8>(bf16);
+      if constexpr (D / 64 >= 8) return pick_combine_ds<KV, D, 8>(bf16, cw);
       return nullptr;
   }
+}
+
+// waves per combine work-group: eight while the launch holds at most
+// kCombineWideGroups work-groups, four above (so that it stays about one
+// round: eight-wave groups over 1024 (sequence, head, part) rows took two)
+inline int combine_waves(int groups) {
+  return groups <= kCombineWideGroups ? kCombineWavesMax : kCombineWavesMax / 2;
 }
 
 inline int default_window(int variant) { return variant == GQA_SLIDING ? kSlidingWindow : 0; }
@@ -1460,7 +1494,12 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ka.max_pages = paged ? max_pages : 0;
   ka.num_pages = paged ? num_pages : 0;
   ka.window = window;
-  ka.n_waves = plan.waves;
+  // stream mode launches one persistent wave per SIMD slot of the variant's
+  // bf16 kernel; the f32 sliding kernel fits one wave per SIMD, so it launches
+  // half as many (one round, the slots it leaves unused stay in the workspace)
+  const int launch_waves =
+      !unit_mode && variant == GQA_SLIDING && !bf16 ? plan.waves / 2 : plan.waves;
+  ka.n_waves = launch_waves;
   ka.ring = ring;
 
   MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(unit_mode, paged, bf16)
@@ -1468,7 +1507,8 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
                                            : pick_main<4, 512, false>(unit_mode, paged, bf16);
   ProfRec* pr = prof_slot(kfv ? kProfKeysFromValues : 2 * variant);
   if (pr) (void)hipEventRecord(pr->start, stream);
-  hipLaunchKernelGGL(main_fn, dim3((unsigned)(plan.waves / kWaves)), dim3(kThreads), 0, stream, ka);
+  hipLaunchKernelGGL(main_fn, dim3((unsigned)(launch_waves / kWaves)), dim3(kThreads), 0, stream,
+                     ka);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (pr) (void)hipEventRecord(pr->stop, stream);
   if (unit_mode) return GQA_OK;
@@ -1479,14 +1519,15 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ca.ws_acc = ka.ws_acc;
   ca.o = ka.o;
   ca.B = B;
-  ca.n_waves = plan.waves;
+  ca.n_waves = launch_waves;
   const int ds = variant == GQA_SLIDING ? combine_parts<256>(B) : combine_parts<512>(B);
+  const int cw = combine_waves(B * kHeads * ds);
   CombineFn comb =
-      variant == GQA_SLIDING ? pick_combine<16, 256>(bf16, ds) : pick_combine<4, 512>(bf16, ds);
+      variant == GQA_SLIDING ? pick_combine<16, 256>(bf16, ds, cw) : pick_combine<4, 512>(bf16, ds, cw);
   if (!comb) return GQA_ERR_SHAPE;
   ProfRec* pc = prof_slot(kfv ? kProfKeysFromValues + 1 : 2 * variant + 1);
   if (pc) (void)hipEventRecord(pc->start, stream);
-  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads * ds)), dim3(64u * kCombineWaves), 0, stream,
+  hipLaunchKernelGGL(comb, dim3((unsigned)(B * kHeads * ds)), dim3(64u * (unsigned)cw), 0, stream,
                      ca);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (pc) (void)hipEventRecord(pc->stop, stream);

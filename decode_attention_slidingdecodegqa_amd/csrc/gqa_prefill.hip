@@ -248,13 +248,16 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     const int ld_c = threadIdx.x % NCH;
     static_assert(DMA || (NT / NCH <= 16 && 16 % (NT / NCH) == 0),
                   "register staging: a thread's rows stay within one 16-row half");
+    const char* const k_base = a.k;
+    const char* const v_base = a.v;
     auto fetch = [&](int step, int& okbits, auto& dst) {
       const int pos0 = step * PT;
-      // K and V rows of the step's 16-row halves (wave-uniform pointers); a
+      // offsets of the step's 16-row halves in the cache (wave-uniform); a
       // page id outside the pool is never dereferenced: its half reads the
-      // library's zero page and its keys are masked in compute()
-      const char* kh[NH];
-      const char* vh[NH];
+      // library's zero page instead (half_ptr) and its keys are masked in
+      // compute().  One offset per half keeps the scalar registers of the
+      // fetch as few as a plain offset needs.
+      size_t base[NH];
       okbits = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
@@ -268,16 +271,19 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int page = __builtin_amdgcn_readlane(bt_lane, pi & 63);
           const bool ok = page >= 0 && page < a.num_pages;
           okbits |= ok ? (1 << h) : 0;
-          const size_t off = ((size_t)page * kPage * KV + g) * (size_t)ROW;
-          kh[h] = ok ? a.k + off : zero_page() + (size_t)g * ROW;
-          vh[h] = ok ? a.v + off : zero_page() + (size_t)g * ROW;
+          base[h] = ((size_t)(ok ? page : 0) * kPage * KV + g) * (size_t)ROW;
         } else {
           okbits |= 1 << h;
-          const size_t off = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
-          kh[h] = a.k + off;
-          vh[h] = a.v + off;
+          base[h] = (((size_t)b * a.cap + pos0 + 16 * h) * KV + g) * (size_t)ROW;
         }
       }
+      // rows of half h of K (which = 0) or V (which = 1); the cache bases are
+      // selected as values (selecting the argument fields themselves made the
+      // compiler copy the argument block to scratch memory)
+      auto half_ptr = [&](int which, int h) -> const char* {
+        if (PAGED && !((okbits >> h) & 1)) return zero_page() + (size_t)g * ROW;
+        return (which ? v_base : k_base) + base[h];
+      };
       if constexpr (DMA) {
         // LDS-DMA through buffer descriptors, one per K/V and 16-row half of
         // the step, each spanning those 16 rows: the row's offset goes in the
@@ -287,8 +293,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
         // operand reads of the step being computed.)
         auto dma = [&](int which, int h, int row_in_half, int part, int lds_off) {
           // the descriptor's base is wave-uniform: keep it in scalar registers
-          const int hh = NH == 1 || h == 0 ? 0 : NH - 1;
-          const uint64_t addr = (uint64_t)(which ? vh[hh] : kh[hh]);
+          const uint64_t addr = (uint64_t)half_ptr(which, NH == 1 || h == 0 ? 0 : NH - 1);
           const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
           const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
           const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -328,9 +333,8 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int which = (RPU * u) / PT;               // 0: K, 1: V
           const int rin = (RPU * u) % PT;                 // + row0 < 16 within its half
           const int h = rin / 16;
-          const int hh = NH == 1 ? 0 : h;
           const size_t off = (size_t)(ld_row0 + rin % 16) * POS + ld_c * 16;
-          ld[u] = load16((which ? vh[hh] : kh[hh]) + off);
+          ld[u] = load16(half_ptr(which, NH == 1 ? 0 : h) + off);
         }
       } else {
 #pragma unroll
@@ -341,9 +345,8 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int c = q % NCH;
           const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
           const int h = rel >> 4;
-          const int hh = NH == 1 ? 0 : (h ? NH - 1 : 0);
           const size_t off = (size_t)(rel & 15) * POS + c * 16;
-          ld[u] = load16((which ? vh[hh] : kh[hh]) + off);
+          ld[u] = load16(half_ptr(which, NH == 1 ? 0 : (h ? NH - 1 : 0)) + off);
         }
       }
     };

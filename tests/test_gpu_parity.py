@@ -58,8 +58,9 @@ def test_parity_batch_shapes(variant):
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 def test_combine_d_parts(variant, dtype):
     # stream mode at batch sizes that give the combine 8, 4, 2 and 1 d parts per head
-    # (fewer than 1024 (sequence, head) rows split each head's D across work-groups);
-    # sliding with a 2048 window, whose 129-tile units keep these batches in stream mode
+    # (fewer than 256 (sequence, head) rows split each head's D across work-groups)
+    # and work-groups of eight and of four waves (above 512 groups); sliding with a
+    # 2048 window, whose 129-tile units keep these batches in stream mode
     cap = SMALL[variant][0]
     window = 2048 if variant == "sliding" else None
     for B in ((1, 2, 5, 16, 24, 31, 33) if dtype == "bf16" else (1, 16, 33)):
@@ -101,13 +102,21 @@ def test_single_position_is_exact(variant, dtype, paged):
             assert torch.equal(got[b, h], exp), (b, h)
 
 
-def slice_boundary_positions(variant, lens, cap):
+def stream_waves(variant, dtype, plan_waves, T):
+    """Waves sharing T tiles in stream mode: the launch (half the plan's waves
+    for the f32 sliding kernel, which fits one wave per SIMD), fewer when T
+    gives global waves fewer than 8 tiles each (at least 256)."""
+    W = plan_waves // 2 if (variant == "sliding" and dtype == "f32") else plan_waves
+    per = 8 if variant == "global" else 1
+    return min(W, max(256, -(-T // per)))
+
+
+def slice_boundary_positions(variant, lens, cap, dtype="bf16"):
     """For each sequence, the first position of a tile that starts a new wave
     slice inside kv head 0's unit (the position where two slices of the
     stream partition meet), or the unit's middle if one slice holds it."""
     KV = 16 if variant == "sliding" else 4
     plan = gqa.gqa_decode_plan(variant, len(lens), cap)
-    W = plan["waves"] if plan["mode"] == "stream" else 1
     rng = []
     for L in lens:
         L = min(L, cap)
@@ -115,6 +124,7 @@ def slice_boundary_positions(variant, lens, cap):
         t0 = lo // 16
         rng.append((lo, L, t0, (L + 15) // 16 - t0))
     T = KV * sum(n for *_, n in rng)
+    W = stream_waves(variant, dtype, plan["waves"], T) if plan["mode"] == "stream" else 1
     out, first = [], 0
     for lo, L, t0, n in rng:
         s0 = first                       # flattened first tile of unit (b, g=0)
@@ -137,7 +147,7 @@ def test_one_hot_dominant_logit_selects_exactly(variant, dtype, paged):
     cap = 1296
     for pick in ("lo", "last", "page0", "page15", "slice"):
         if pick == "slice":
-            pos = slice_boundary_positions(variant, lens, cap)
+            pos = slice_boundary_positions(variant, lens, cap, dtype)
         else:
             pos = []
             for L in lens:
