@@ -138,11 +138,26 @@ struct RopeLds {
 // by bit 3, so neither has bank conflicts (a 16-byte row pad halves both).
 template <bool KFV, bool BF16>
 constexpr bool kStaged = KFV && BF16;
+// bf16 stored keys: each tile's key rows are fetched whole (one 1 KiB load
+// instruction per 1 KiB of rows, the pattern a plain read streams fastest)
+// and reach the MFMA operand layout (lane (r, j): row r, chunks 4c + j)
+// through a per-wave LDS tile of unpadded rows with the same chunk swizzle.
+// Fetched in the operand layout directly, every load instruction took 64
+// bytes of 16 rows: a plain read in that pattern measured 6.0 TB/s, whole
+// rows 7.37 TB/s, and the value rows' pattern (4 rows x 256 bytes) 7.1.
+template <bool KFV, bool BF16>
+constexpr bool kRowKeys = !KFV && BF16;
 constexpr int kStageRow = 512 * 2;
 __device__ __forceinline__ int stage_swz(int r) { return ((r & 3) << 2) | ((r & 4) >> 1); }
 constexpr int kStageTileBytes = kTile * kStageRow;
 // followed by the rebuilt key chunks: 4 slots x 64 lanes x 16 bytes
 constexpr int kStageBytes = kStageTileBytes + 4 * 64 * 16;
+// LDS bytes per wave of a main kernel: the keys-from-values tile, the
+// whole-row keys' tile (16 rows of ROW bytes), or none
+template <bool KFV, bool BF16, int ROW>
+constexpr int wave_stage_bytes() {
+  return kStaged<KFV, BF16> ? kStageBytes : kRowKeys<KFV, BF16> ? kTile * ROW : 0;
+}
 
 template <bool BF16>
 __device__ inline float elem_f32(const char* base, int i) {
@@ -311,12 +326,38 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     return p - pos0;
   };
 
-  u32x4 kreg[KCH];      // key row r of the tile, chunks 4t+j
+  constexpr bool ROWK = kRowKeys<KFV, BF16>;
+  // whole-row key fetch: instruction c takes the 1 KiB of tile rows
+  // RPI*c .. RPI*c + RPI-1, lane l its 16-byte chunk l % NCH of row
+  // RPI*c + l / NCH (KCH instructions either way: the same registers)
+  constexpr int RPI = 1024 / ROW > 0 ? 1024 / ROW : 1;  // rows per load instruction
+  auto krow_of = [&](int c) { return RPI * c + lane / NCH; };
+  u32x4 kreg[KCH];      // key row r of the tile, chunks 4t+j (ROWK: the raw rows)
   u32x4 vreg[4][VBLK];  // value rows 4j+i of the tile, chunks r+16*blk
   auto load_k = [&](const TileAt& ta) {
-    const char* row = ta.kb + (size_t)clamp_row(ta.pos0, r) * POS;
+    if constexpr (ROWK) {
+      static_assert(KCH * 64 * 16 == kTile * ROW, "whole-row key fetch: one register per chunk");
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) kreg[c] = load16(row + (4 * c + j) * 16);
+      for (int c = 0; c < KCH; ++c)
+        kreg[c] = load16_stream(ta.kb + (size_t)clamp_row(ta.pos0, krow_of(c)) * POS +
+                                16 * (lane % NCH));
+    } else {
+      const char* row = ta.kb + (size_t)clamp_row(ta.pos0, r) * POS;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) kreg[c] = load16(row + (4 * c + j) * 16);
+    }
+  };
+  // the raw key rows into the wave's LDS tile (row-major, ROW bytes a row,
+  // chunk p of row q at p ^ stage_swz(q)); written a whole row range per
+  // instruction, so the writes are free of bank conflicts
+  auto stage_keys = [&]() {
+    if constexpr (ROWK) {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int q = krow_of(c);
+        *reinterpret_cast<u32x4*>(stage + q * ROW + 16 * ((lane % NCH) ^ stage_swz(q))) = kreg[c];
+      }
+    }
   };
   auto load_v = [&](const TileAt& ta) {
 #pragma unroll
@@ -421,7 +462,9 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   };
   // the QK^T operand chunk c of the lane (compile-time c)
   auto key_op = [&](int c) -> u32x4 {
-    if constexpr (STAGED) {
+    if constexpr (ROWK) {
+      return *reinterpret_cast<const u32x4*>(stage + r * ROW + 16 * ((4 * c + j) ^ stage_swz(r)));
+    } else if constexpr (STAGED) {
       if (c < TA) return rot[c * 64 + lane];
       if (c >= TP && c < TP + TA) return rot[(TA + c - TP) * 64 + lane];
       return *reinterpret_cast<const u32x4*>(stage + r * kStageRow +
@@ -468,6 +511,13 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       if (more) load_k(nxt);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+    } else if constexpr (ROWK) {
+      // this tile's key rows into the wave's LDS tile, then the registers
+      // take the next tile's rows at once (fetched a whole QK^T earlier)
+      stage_keys();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (more) load_k(nxt);
     } else {
       rebuild_keys(kreg);
     }
@@ -518,7 +568,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
         for (int blk = 0; blk < VBLK; ++blk)
           vreg[i][blk] = *reinterpret_cast<const u32x4*>(
               stage + (4 * j + i) * kStageRow + 16 * ((r ^ stage_swz(4 * j + i)) + 16 * blk));
-    } else {
+    } else if constexpr (!ROWK) {
       // the key registers are free: fetch the next tile's keys
       if (more) load_k(nxt);
     }
@@ -642,9 +692,9 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ u32x4 s_q[kWaves][G * NCH];   // per-wave query heads of the current unit
   __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
   RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
-  constexpr bool STAGED = kStaged<KFV, BF16>;
-  __shared__ __attribute__((aligned(16))) char s_stage[STAGED ? kWaves * kStageBytes : 16];
-  char* stage = STAGED ? s_stage + (threadIdx.x >> 6) * kStageBytes : nullptr;
+  constexpr int SB = wave_stage_bytes<KFV, BF16, ROW>();  // per wave
+  __shared__ __attribute__((aligned(16))) char s_stage[SB > 0 ? kWaves * SB : 16];
+  char* stage = SB > 0 ? s_stage + (threadIdx.x >> 6) * SB : nullptr;
   if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
   if (threadIdx.x < 64) {
     int cnt[4];
@@ -755,9 +805,9 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ u32x4 s_q[kWaves][G * NCH];
   // the merge rows of waves 1..3; the staged path's per-wave tiles share the
   // space (every wave has left its tile loop before the merge writes)
-  constexpr bool STAGED = kStaged<KFV, BF16>;
+  constexpr int SB = wave_stage_bytes<KFV, BF16, ROW>();  // per wave
   constexpr int ACC_BYTES = (kWaves - 1) * G * LROW * 4;
-  constexpr int POOL = STAGED && kWaves * kStageBytes > ACC_BYTES ? kWaves * kStageBytes : ACC_BYTES;
+  constexpr int POOL = kWaves * SB > ACC_BYTES ? kWaves * SB : ACC_BYTES;
   __shared__ __attribute__((aligned(16))) char s_pool[POOL];
   float* s_acc = reinterpret_cast<float*>(s_pool);
   __shared__ float s_m[(kWaves - 1) * G];
@@ -786,8 +836,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
 
   WaveState<KV, D, BF16> st;
   accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, wave, sr.n, kWaves, s_q[wave], s_rope,
-                                            STAGED ? s_pool + wave * kStageBytes : nullptr, st);
-  if constexpr (STAGED) __syncthreads();  // the tiles are dead before s_acc is written
+                                            SB > 0 ? s_pool + wave * SB : nullptr, st);
+  if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
 
   if (wave > 0 && r < G) {
     float* dst = s_acc + ((wave - 1) * G + r) * LROW;
@@ -1834,7 +1884,9 @@ int gqa_hbm_read_probe(const void* src, size_t bytes, void* sink, void* stream) 
   if (!src || !sink) return GQA_ERR_NULL;
   if (bytes == 0 || bytes % 16) return GQA_ERR_SHAPE;
   if (!aligned16(src)) return GQA_ERR_ALIGN;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(2048), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+  // 1024 waves (one per SIMD), 8 KiB in flight each: the fastest plain read
+  // of a sweep over wave counts and depths (8192 waves read about 4% slower)
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), bytes / 16, static_cast<unsigned*>(sink));
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
