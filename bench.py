@@ -252,6 +252,54 @@ class Timer:
             t.append(a.elapsed_time(b) * 1e3)
         return statistics.median(t)
 
+    def queued(self, call, n):
+        """Median of n flushed single calls, each queued behind its flush with
+        no host synchronisation in between: the call's launch (host) cost is
+        hidden behind the flush, as behind the previous layer's work in a
+        decode step, so the span is the call's own device latency with cold
+        caches."""
+        torch = self.torch
+        if self.flush_buf is None:
+            self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=self.dev)
+        t = []
+        for _ in range(n):
+            a, b = self._ev(), self._ev()
+            self.flush_buf.sum()
+            a.record(self.stream)
+            call()
+            b.record(self.stream)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(t)
+
+    def graph(self, call, reps):
+        """Mean per call of `reps` back-to-back calls replayed from one HIP
+        graph (captured once, replayed three times, the last two timed): the
+        device time per call with no host launch cost in the loop."""
+        torch = self.torch
+        side = torch.cuda.Stream(self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = self._ev(), self._ev()
+        a.record(self.stream)
+        g.replay()
+        g.replay()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        del g
+        us = a.elapsed_time(b) / (2 * reps) * 1e3
+        if us < 1.0:  # a call launched outside the capture stream ran eagerly
+            raise RuntimeError(f"the captured graph holds no decode work ({us:.2f} us per call)")
+        return us
+
     def release(self):
         self.flush_buf = None
 
@@ -296,22 +344,24 @@ class Ctx:
         return self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=self.dev)
 
     def decode_call(self, c, o, ws, window=None):
+        """The call on the current stream (self.stream outside a graph capture,
+        the capture stream inside one)."""
         gqa = self.gqa
         if window is not None:
             if c.block_table is None:
                 return lambda: gqa.gqa_decode_sliding_window(c.q, c.k, c.v, c.seq_lens, window,
                                                              o=o, workspace=ws,
-                                                             stream=self.stream)
+                                                             stream=None)
             return lambda: gqa.gqa_decode_sliding_window_paged(c.q, c.k, c.v, c.block_table,
                                                                c.seq_lens, window, o=o,
-                                                               workspace=ws, stream=self.stream)
+                                                               workspace=ws, stream=None)
         fn = {("sliding", False): gqa.gqa_decode_sliding, ("global", False): gqa.gqa_decode_global,
               ("sliding", True): gqa.gqa_decode_sliding_paged,
               ("global", True): gqa.gqa_decode_global_paged}[(c.variant, c.paged)]
         if c.paged:
             return lambda: fn(c.q, c.k, c.v, c.block_table, c.seq_lens, o=o, workspace=ws,
-                              stream=self.stream)
-        return lambda: fn(c.q, c.k, c.v, c.seq_lens, o=o, workspace=ws, stream=self.stream)
+                              stream=None)
+        return lambda: fn(c.q, c.k, c.v, c.seq_lens, o=o, workspace=ws, stream=None)
 
 
 def section_step(ctx, line):
@@ -404,6 +454,8 @@ def section_small(ctx, line):
             call()
         warm = ctx.timer.warm(call, 20)
         cold = ctx.timer.single(call, n)
+        queued = ctx.timer.queued(call, n)
+        graph = ctx.timer.graph(call, 20)
         # kernel durations from the library's events, in a separate flushed pass
         # (the events add gaps between the launches of a call)
         gqa.profile_begin(2 * min(n, 20) + 4)
@@ -418,9 +470,13 @@ def section_small(ctx, line):
             "kv_GBps_after_flush": gbps(nb, cold), "frac_of_hbm_peak_after_flush": frac(nb, cold),
             "main_kernel_us_after_flush": round(main_us, 2),
             "combine_kernel_us_after_flush": round(comb_us, 2),
-            "us_per_call_warm": round(warm, 2), "frac_of_hbm_peak_warm": frac(nb, warm)}
+            "us_per_call_after_flush_queued_median": round(queued, 2),
+            "us_per_call_warm": round(warm, 2), "frac_of_hbm_peak_warm": frac(nb, warm),
+            "us_per_call_graph": round(graph, 2), "frac_of_hbm_peak_graph": frac(nb, graph)}
         line["config"][f"{key}_{name}_us"] = round(cold, 2)
         line["config"][f"{key}_{name}_frac"] = frac(nb, cold)
+        line["config"][f"{key}_{name}_us_graph"] = round(graph, 2)
+        line["config"][f"{key}_{name}_us_after_flush_queued"] = round(queued, 2)
         del c, o
 
 
@@ -547,6 +603,8 @@ def section_long(ctx, line):
             call()
         warm = ctx.timer.warm(call, 20)
         cold = ctx.timer.single(call, n)
+        queued = ctx.timer.queued(call, n)
+        graph = ctx.timer.graph(call, 20)
         gqa.profile_begin(48)
         ctx.timer.warm(call, 20)
         main_w, comb_w = kernel_us(gqa.profile_read(), c.variant)
@@ -556,10 +614,14 @@ def section_long(ctx, line):
                     "frac_of_hbm_peak": frac(nb, warm), "main_kernel_us": round(main_w, 2),
                     "combine_kernel_us": round(comb_w, 2),
                     "us_per_call_after_flush_median": round(cold, 2),
-                    "frac_of_hbm_peak_after_flush": frac(nb, cold)}
+                    "frac_of_hbm_peak_after_flush": frac(nb, cold),
+                    "us_per_call_after_flush_queued_median": round(queued, 2),
+                    "us_per_call_graph": round(graph, 2), "frac_of_hbm_peak_graph": frac(nb, graph)}
         key = "c4_global" if c.variant == "global" else "c4_sliding"
         line["config"][f"{key}_b1_s262144_us"] = round(warm, 2)
         line["config"][f"{key}_b1_s262144_us_after_flush"] = round(cold, 2)
+        line["config"][f"{key}_b1_s262144_us_graph"] = round(graph, 2)
+        line["config"][f"{key}_b1_s262144_us_after_flush_queued"] = round(queued, 2)
         line["config"][f"{key}_b1_s262144_frac"] = frac(nb, warm)
         del c, o
     line["config"]["single_sequence_262144"] = b1

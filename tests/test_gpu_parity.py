@@ -104,11 +104,10 @@ def test_single_position_is_exact(variant, dtype, paged):
 
 def stream_waves(variant, dtype, plan_waves, T):
     """Waves sharing T tiles in stream mode: the launch (half the plan's waves
-    for the f32 sliding kernel, which fits one wave per SIMD), fewer when T
-    gives global waves fewer than 8 tiles each (at least 256)."""
+    for the f32 sliding kernel, which fits one wave per SIMD), only
+    max(T, 256) of them when T is smaller."""
     W = plan_waves // 2 if (variant == "sliding" and dtype == "f32") else plan_waves
-    per = 8 if variant == "global" else 1
-    return min(W, max(256, -(-T // per)))
+    return min(W, max(256, T))
 
 
 def slice_boundary_positions(variant, lens, cap, dtype="bf16"):
