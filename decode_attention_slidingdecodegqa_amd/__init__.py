@@ -42,6 +42,7 @@ from ._lib import (  # noqa: F401
     GQA_SLIDING,
     GqaError,
     constants,
+    force_mode,
     gqa_append_global,
     gqa_append_global_k_eq_v,
     gqa_append_sliding,

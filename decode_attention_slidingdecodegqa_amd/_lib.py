@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "gqa_prefill_sliding_paged", "gqa_prefill_global_paged", "gqa_decode_sliding_ring",
     "gqa_decode_sliding_ring_workspace_bytes", "gqa_append_sliding_ring",
     "gqa_prefill_sliding_window", "gqa_prefill_sliding_window_paged",
-    "gqa_decode_global_paged_noalloc",
+    "gqa_decode_global_paged_noalloc", "gqa_decode_force_mode",
 )
 
 
@@ -56,6 +56,8 @@ def library():
                        ("gqa_decode_sliding_paged", paged), ("gqa_decode_global_paged", paged)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lib.gqa_decode_force_mode.argtypes = [i32]
+    lib.gqa_decode_force_mode.restype = ctypes.c_int
     lib.gqa_decode_global_paged_noalloc.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, p]
     lib.gqa_decode_global_paged_noalloc.restype = ctypes.c_int
     lib.gqa_decode_sliding_window.argtypes = [p, p, p, p, p, i32, i32, i32, i32, p, sz, p]
@@ -144,11 +146,12 @@ def gqa_decode_workspace_bytes(variant, B: int, capacity: int, window: int | Non
     return int(library().gqa_decode_workspace_bytes(_variant(variant), int(B), int(capacity)))
 
 
-GQA_MODE_UNIT, GQA_MODE_STREAM = 0, 1
+GQA_MODE_UNIT, GQA_MODE_STREAM, GQA_MODE_GROUP = 0, 1, 2
+_MODE_NAMES = {GQA_MODE_UNIT: "unit", GQA_MODE_STREAM: "stream", GQA_MODE_GROUP: "group"}
 
 
 def gqa_decode_plan(variant, B: int, capacity: int, window: int | None = None) -> dict:
-    """Launch plan: {'mode': 'unit'|'stream', 'waves': W, 'slots': workspace slots}."""
+    """Launch plan: {'mode': 'unit'|'stream'|'group', 'waves': W, 'slots': workspace slots}."""
     mode, n, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     if window is not None:
         if _variant(variant) != GQA_SLIDING:
@@ -161,8 +164,17 @@ def gqa_decode_plan(variant, B: int, capacity: int, window: int | None = None) -
                                        ctypes.byref(mode), ctypes.byref(n), ctypes.byref(t))
     if rc:
         raise GqaError("gqa_decode_plan", rc)
-    return {"mode": "unit" if mode.value == GQA_MODE_UNIT else "stream", "waves": n.value,
-            "slots": t.value}
+    return {"mode": _MODE_NAMES[mode.value], "waves": n.value, "slots": t.value}
+
+
+def force_mode(mode: str | None) -> None:
+    """Make later plans and calls take launch mode 'unit', 'stream' or 'group'
+    whatever the planner would choose (None: the planner's choice again).
+    Process-wide; for measurement and tests."""
+    code = -1 if mode is None else {v: k for k, v in _MODE_NAMES.items()}[mode]
+    rc = library().gqa_decode_force_mode(code)
+    if rc:
+        raise GqaError("gqa_decode_force_mode", rc)
 
 
 def profile_begin(capacity: int) -> None:

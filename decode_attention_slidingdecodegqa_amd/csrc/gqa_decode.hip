@@ -673,6 +673,47 @@ __device__ __forceinline__ void store_partial(const WaveState<KV, D, BF16>& st, 
   }
 }
 
+// Tile counts of every sequence (s_cnt: tiles per unit), their lengths and
+// the exclusive prefix sums of the counts (s_before[B]: the total), in LDS;
+// work-group 0 also writes the prefix times KV to a.prefix for the combine.
+// Called by wave 0 (lane l takes sequences 4l .. 4l+3); the caller then syncs.
+template <int KV>
+__device__ inline void tile_prefix(const KernelArgs& a, int* s_len, int* s_cnt, int* s_before) {
+  const int lane = threadIdx.x & 63;
+  int cnt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * lane + i;
+    const int L = b < a.B ? a.seq_lens[b] : 0;
+    cnt[i] = seq_range(L, position_cap(a.cap, a.ring), a.window).n;
+    if (b < a.B) {
+      s_len[b] = L;
+      s_cnt[b] = cnt[i];
+    }
+  }
+  const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  int incl = lsum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  int run_b = incl - lsum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * lane + i;
+    if (b < a.B) {
+      s_before[b] = run_b;
+      if (blockIdx.x == 0) a.prefix[b] = KV * run_b;
+    }
+    run_b += cnt[i];
+  }
+  if (lane == 63) {
+    s_before[a.B] = incl;
+    if (blockIdx.x == 0) a.prefix[a.B] = KV * incl;
+  }
+}
+
 // ---- stream kernel: W persistent waves, each an equal slice of all tiles
 template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_stream_kernel(
@@ -696,40 +737,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ __attribute__((aligned(16))) char s_stage[SB > 0 ? kWaves * SB : 16];
   char* stage = SB > 0 ? s_stage + (threadIdx.x >> 6) * SB : nullptr;
   if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
-  if (threadIdx.x < 64) {
-    int cnt[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * lane + i;
-      const int L = b < a.B ? a.seq_lens[b] : 0;
-      cnt[i] = seq_range(L, position_cap(a.cap, a.ring), a.window).n;
-      if (b < a.B) {
-        s_len[b] = L;
-        s_cnt[b] = cnt[i];
-      }
-    }
-    const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    int incl = lsum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    int run_b = incl - lsum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * lane + i;
-      if (b < a.B) {
-        s_before[b] = run_b;
-        if (blockIdx.x == 0) a.prefix[b] = KV * run_b;
-      }
-      run_b += cnt[i];
-    }
-    if (lane == 63) {
-      s_before[a.B] = incl;
-      if (blockIdx.x == 0) a.prefix[a.B] = KV * incl;
-    }
-  }
+  if (threadIdx.x < 64) tile_prefix<KV>(a, s_len, s_cnt, s_before);
   __syncthreads();
   const long T = (long)KV * s_before[a.B];  // tiles of all units
 
@@ -794,13 +802,79 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   }
 }
 
+// The four waves' states of one unit merged through LDS: waves 1..3 write
+// their O rows and (m, l), and wave 0's lanes r < G fold them into their own
+// state in place (st.m becomes the common reference max, Lt the total
+// weight).  Returns true on those lanes, which alone hold the merged state.
+// Every wave of the work-group calls it (it holds a barrier); s_acc holds
+// 3 G rows of D + 4 floats, s_m and s_l 3 G floats.
+template <int KV, int D, bool BF16>
+__device__ __forceinline__ bool merge_group(WaveState<KV, D, BF16>& st, float* s_acc, float* s_m,
+                                            float* s_l, float& Lt) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, E = Gm::E, VBLK = Gm::VBLK;
+  constexpr int LROW = D + 4;  // padded LDS row (floats)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  if (wave > 0 && r < G) {
+    float* dst = s_acc + ((wave - 1) * G + r) * LROW;
+#pragma unroll
+    for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[16 * E * blk + 4 * E * j + E * i + e] = st.acc[blk][e][i];
+    if (j == 0) {
+      s_m[(wave - 1) * G + r] = st.m;
+      s_l[(wave - 1) * G + r] = st.l;
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || r >= G) return false;
+
+  float M = st.m;
+  float mw[kWaves - 1], lw[kWaves - 1];
+#pragma unroll
+  for (int v = 0; v < kWaves - 1; ++v) {
+    mw[v] = s_m[v * G + r];
+    lw[v] = s_l[v * G + r];
+    M = fmaxf(M, mw[v]);
+  }
+  const float Muse = M == -INFINITY ? 0.f : M;
+  const float sc0 = exp2_fast((st.m - Muse) * kLog2e);
+  float sc[kWaves - 1];
+  Lt = sc0 * st.l;
+#pragma unroll
+  for (int v = 0; v < kWaves - 1; ++v) {
+    sc[v] = exp2_fast((mw[v] - Muse) * kLog2e);
+    Lt += sc[v] * lw[v];
+  }
+#pragma unroll
+  for (int blk = 0; blk < VBLK; ++blk)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      f32x4 x = sc0 * st.acc[blk][e];
+#pragma unroll
+      for (int v = 0; v < kWaves - 1; ++v) {
+        const float* row = s_acc + (v * G + r) * LROW + 16 * E * blk + 4 * E * j + e;
+        x += sc[v] * f32x4{row[0], row[E], row[2 * E], row[3 * E]};
+      }
+      st.acc[blk][e] = x;
+    }
+  st.m = M;
+  st.l = Lt;
+  return true;
+}
+
 // ---- unit kernel: one work-group per unit (many short units); its four
 // waves take interleaved tiles and merge their states in LDS, then write o
 template <int KV, int D, bool PAGED, bool BF16, bool KFV>
 __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_unit_kernel(
     KernelArgs a) {
   using Gm = Geo<KV, D, BF16>;
-  constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, VBLK = Gm::VBLK;
+  constexpr int G = Gm::G, ROW = Gm::ROW, NCH = Gm::NCH;
   constexpr int LROW = D + 4;  // padded LDS row (floats)
   __shared__ u32x4 s_q[kWaves][G * NCH];
   // the merge rows of waves 1..3; the staged path's per-wave tiles share the
@@ -819,10 +893,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
     __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const int j = lane >> 4;
+  const int r = threadIdx.x & 15;
   const int unit = blockIdx.x;
   const int b = unit / KV;
   const int g = unit % KV;
@@ -839,54 +911,124 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
                                             SB > 0 ? s_pool + wave * SB : nullptr, st);
   if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
 
-  if (wave > 0 && r < G) {
-    float* dst = s_acc + ((wave - 1) * G + r) * LROW;
-#pragma unroll
-    for (int blk = 0; blk < VBLK; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < E; ++e) dst[16 * E * blk + 4 * E * j + E * i + e] = st.acc[blk][e][i];
-    if (j == 0) {
-      s_m[(wave - 1) * G + r] = st.m;
-      s_l[(wave - 1) * G + r] = st.l;
-    }
-  }
-  __syncthreads();
-  if (wave != 0 || r >= G) return;
-
-  float M = st.m;
-  float mw[kWaves - 1], lw[kWaves - 1];
-#pragma unroll
-  for (int v = 0; v < kWaves - 1; ++v) {
-    mw[v] = s_m[v * G + r];
-    lw[v] = s_l[v * G + r];
-    M = fmaxf(M, mw[v]);
-  }
-  const float Muse = M == -INFINITY ? 0.f : M;
-  const float sc0 = exp2_fast((st.m - Muse) * kLog2e);
-  float sc[kWaves - 1];
-  float Lt = sc0 * st.l;
-#pragma unroll
-  for (int v = 0; v < kWaves - 1; ++v) {
-    sc[v] = exp2_fast((mw[v] - Muse) * kLog2e);
-    Lt += sc[v] * lw[v];
-  }
-  WaveState<KV, D, BF16> mg;
-#pragma unroll
-  for (int blk = 0; blk < VBLK; ++blk)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      f32x4 x = sc0 * st.acc[blk][e];
-#pragma unroll
-      for (int v = 0; v < kWaves - 1; ++v) {
-        const float* row = s_acc + (v * G + r) * LROW + 16 * E * blk + 4 * E * j + e;
-        x += sc[v] * f32x4{row[0], row[E], row[2 * E], row[3 * E]};
-      }
-      mg.acc[blk][e] = x;
-    }
+  float Lt;
+  if (!merge_group<KV, D, BF16>(st, s_acc, s_m, s_l, Lt)) return;
   const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  store_o<KV, D, BF16>(mg, a.o + ((size_t)b * kHeads + g * G + r) * ROW, inv);
+  store_o<KV, D, BF16>(st, a.o + ((size_t)b * kHeads + g * G + r) * ROW, inv);
+}
+
+// ---- group kernel: the stream partition over work-groups
+// Work-group w takes the equal slice [w*T/NG, (w+1)*T/NG) of the flattened
+// tiles; its four waves share each unit piece of the slice tile by tile (wave
+// i takes the piece's tiles i, i+4, ...) and merge their states in LDS.  A
+// piece that is a whole unit writes o; otherwise the work-group writes the
+// merged partial to slot unit + w, and the combine kernel merges the
+// partials as in stream mode (with the work-groups in the place of the
+// waves).  A work-group's partial stands for four waves' tiles, so the
+// workspace traffic is a quarter of stream mode's at the same parallelism.
+
+// Work-groups that share the T tiles of a grouped call: the NG launched, or
+// fewer when the lengths give fewer than kWaves tiles per work-group (every
+// remaining slice then holds at least one tile).
+__device__ inline int effective_groups(long T, int NG) {
+  const long need = (T + kWaves - 1) / kWaves;
+  return need < NG ? (int)(need > 1 ? need : 1) : NG;
+}
+
+template <int KV, int D, bool PAGED, bool BF16, bool KFV>
+__global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void gqa_group_kernel(
+    KernelArgs a) {
+  using Gm = Geo<KV, D, BF16>;
+  constexpr int G = Gm::G, ROW = Gm::ROW, NCH = Gm::NCH;
+  constexpr int LROW = D + 4;  // padded LDS row (floats)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int grp = blockIdx.x;
+
+  __shared__ int s_len[kMaxBatch];
+  __shared__ int s_cnt[kMaxBatch];
+  __shared__ int s_before[kMaxBatch + 1];
+  __shared__ u32x4 s_q[kWaves][G * NCH];
+  // the per-wave tiles and the merge rows of waves 1..3 share the space (the
+  // tile loops of a piece end before its merge writes, and a barrier ends
+  // the merge before the next piece's tiles)
+  constexpr int SB = wave_stage_bytes<KFV, BF16, ROW>();  // per wave
+  constexpr int ACC_BYTES = (kWaves - 1) * G * LROW * 4;
+  constexpr int POOL = kWaves * SB > ACC_BYTES ? kWaves * SB : ACC_BYTES;
+  __shared__ __attribute__((aligned(16))) char s_pool[POOL];
+  float* s_acc = reinterpret_cast<float*>(s_pool);
+  __shared__ float s_m[(kWaves - 1) * G];
+  __shared__ float s_l[(kWaves - 1) * G];
+  __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
+  RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
+  if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
+  if (threadIdx.x < 64) tile_prefix<KV>(a, s_len, s_cnt, s_before);
+  __syncthreads();
+  const long T = (long)KV * s_before[a.B];  // tiles of all units
+
+  // (sequences with nothing attended get their zero rows from the combine)
+  if (T == 0) return;
+  const int NG = effective_groups(T, a.n_waves / kWaves);
+  if (grp >= NG) return;
+  const long s_begin = (long)grp * T / NG;
+  const long s_end = (long)(grp + 1) * T / NG;
+
+  // the sequence holding s_begin: the last one whose first tile is <= s_begin
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = a.B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if ((long)KV * s_before[mid] <= s_begin) lo_b = mid;
+      else hi_b = mid - 1;
+    }
+    b = lo_b;
+  }
+  int n = s_cnt[b];
+  int g, kk0;
+  {
+    const int rel = (int)(s_begin - (long)KV * s_before[b]);
+    g = rel / n;
+    kk0 = rel % n;
+  }
+
+  long t = s_begin;
+  while (t < s_end) {
+    // ---- one piece: tiles [k_begin, k_end) of unit (b, g), shared by the waves
+    const SeqRange sr = seq_range(s_len[b], position_cap(a.cap, a.ring), a.window);
+    const int k_begin = kk0;
+    const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
+    WaveState<KV, D, BF16> st;
+    accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin + wave, k_end, kWaves,
+                                              s_q[wave], s_rope,
+                                              SB > 0 ? s_pool + wave * SB : nullptr, st);
+    if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
+    float Lt;
+    const bool holder = merge_group<KV, D, BF16>(st, s_acc, s_m, s_l, Lt);
+    const int unit = b * KV + g;
+    if (k_begin == 0 && k_end == n) {
+      if (holder) store_o<KV, D, BF16>(st, a.o + ((size_t)b * kHeads + g * G + r) * ROW,
+                                       Lt > 0.f ? 1.f / Lt : 0.f);
+    } else if (holder) {
+      const size_t slot = (size_t)unit + grp;
+      store_partial<KV, D, BF16>(st, a.ws_acc + (slot * G + r) * D);
+      if (j == 0) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + r) * 2) = f32x2{st.m, Lt};
+    }
+    __syncthreads();  // the merge rows are reused by the next piece
+
+    // ---- next unit (skipping sequences with nothing attended)
+    t += k_end - k_begin;
+    kk0 = 0;
+    if (++g == KV) {
+      g = 0;
+      do {
+        ++b;
+      } while (b < a.B && s_cnt[b] == 0);
+    }
+    if (t < s_end) n = s_cnt[b];
+  }
 }
 
 struct CombineArgs {
@@ -895,7 +1037,8 @@ struct CombineArgs {
   const float* ws_acc;
   char* o;
   int32_t B;
-  int32_t n_waves;
+  int32_t n_waves;  // stream mode: the main kernel's waves; group mode: its work-groups
+  int32_t groups;   // nonzero in group mode (slices per work-group, not per wave)
 };
 
 // One work-group of CW waves (8, or 4 when that many work-groups would not
@@ -987,7 +1130,7 @@ __global__ __launch_bounds__(64 * CW) void gqa_combine_kernel(CombineArgs a) {
     return;
   }
   const long s0 = P0 + (long)g * n;
-  const int W = effective_waves(T, a.n_waves);
+  const int W = a.groups ? effective_groups(T, a.n_waves) : effective_waves(T, a.n_waves);
   const int wf = wave_of(s0, T, W);
   const int wl = wave_of(s0 + n - 1, T, W);
   if (wf == wl) return;  // written by the wave that held the whole unit
@@ -1310,9 +1453,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch plan, a function of (variant, B, capacity) only.  Enough short units
 // fill the GPU one work-group per unit and need no workspace; otherwise the
-// stream partition runs with workspace
+// stream partition (over waves, or over work-groups on the global geometry)
+// runs with workspace
 //   [prefix: B+1 int32][ml: slots x G x 2 fp32][acc: slots x G x D fp32],
-// slots = B*KV + W (a slice's partial of unit u sits in slot u + wave).
+// slots = B*KV + W (a slice's partial of unit u sits in slot u + slice, W
+// the waves or work-groups).
 //
 // Unit mode's time is set by its longest unit (a quarter of its tiles per
 // wave, one after another), stream mode's by the bytes plus a combine, so
@@ -1344,6 +1489,10 @@ struct Plan {
 };
 
 // window: attended positions per sequence (0 = every position below L)
+// Launch mode forced for measurement and tests (gqa_decode_force_mode), or -1
+// for the planner's choice.
+int g_force_mode = -1;
+
 int make_plan(int variant, int B, int cap, int window, Plan* P) {
   VariantInfo vi;
   if (!variant_info(variant, &vi)) return GQA_ERR_DTYPE;
@@ -1356,15 +1505,23 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   }
   const int units = B * vi.KV;
   *P = Plan{};
-  if (unit_mode_fits(units, tiles_max, vi.D)) {
+  // split units: work-group slices on the global geometry, wave slices on
+  // the sliding one (group mode, same box: global B=4 25.9 against 28.4 us,
+  // B=1 320 against 327, B=32 and the values-only call equal; sliding bf16
+  // B=1 equal, sliding f32 B=4 34.0 against 31.0)
+  int mode = unit_mode_fits(units, tiles_max, vi.D)
+                 ? GQA_MODE_UNIT
+                 : (variant == GQA_GLOBAL ? GQA_MODE_GROUP : GQA_MODE_STREAM);
+  if (g_force_mode >= 0) mode = g_force_mode;
+  if (mode == GQA_MODE_UNIT) {
     P->mode = GQA_MODE_UNIT;
     P->waves = units * kWaves;
     return GQA_OK;
   }
   const int G = kHeads / vi.KV;
-  P->mode = GQA_MODE_STREAM;
+  P->mode = mode;
   P->waves = vi.waves;
-  P->slots = units + vi.waves;
+  P->slots = units + (mode == GQA_MODE_GROUP ? vi.waves / kWaves : vi.waves);
   P->prefix = 0;
   P->ml = align256((size_t)(B + 1) * sizeof(int32_t));
   P->acc = P->ml + align256((size_t)P->slots * G * 2 * sizeof(float));
@@ -1433,11 +1590,16 @@ typedef void (*MainFn)(KernelArgs);
 typedef void (*CombineFn)(CombineArgs);
 
 template <int KV, int D, bool KFV>
-MainFn pick_main(bool unit_mode, bool paged, bool bf16) {
-  if (unit_mode) {
+MainFn pick_main(int mode, bool paged, bool bf16) {
+  if (mode == GQA_MODE_UNIT) {
     if (paged)
       return bf16 ? gqa_unit_kernel<KV, D, true, true, KFV> : gqa_unit_kernel<KV, D, true, false, KFV>;
     return bf16 ? gqa_unit_kernel<KV, D, false, true, KFV> : gqa_unit_kernel<KV, D, false, false, KFV>;
+  }
+  if (mode == GQA_MODE_GROUP) {
+    if (paged)
+      return bf16 ? gqa_group_kernel<KV, D, true, true, KFV> : gqa_group_kernel<KV, D, true, false, KFV>;
+    return bf16 ? gqa_group_kernel<KV, D, false, true, KFV> : gqa_group_kernel<KV, D, false, false, KFV>;
   }
   if (paged)
     return bf16 ? gqa_stream_kernel<KV, D, true, true, KFV> : gqa_stream_kernel<KV, D, true, false, KFV>;
@@ -1513,18 +1675,19 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   int rc = make_plan(variant, B, ring ? kMaxSeq : cap, window, &plan);
   if (rc) return rc;
   const bool unit_mode = plan.mode == GQA_MODE_UNIT;
+  const bool group_mode = plan.mode == GQA_MODE_GROUP;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   if (!unit_mode) {
     if (workspace_from_scratch) {
       // every host check above has passed: only now is HIP asked for the array
       if (plan.total > kScratchBytes) return GQA_ERR_WORKSPACE;
-      workspace = scratch_address(reinterpret_cast<hipStream_t>(stream_));
+      workspace = scratch_address(stream);
       if (workspace == nullptr) return GQA_ERR_HIP;
       workspace_bytes_given = kScratchBytes;
     }
     if (!workspace || workspace_bytes_given < plan.total) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_ALIGN;
   }
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const bool bf16 = dtype == GQA_BF16;
   char* ws = static_cast<char*>(workspace);
 
@@ -1544,17 +1707,18 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ka.max_pages = paged ? max_pages : 0;
   ka.num_pages = paged ? num_pages : 0;
   ka.window = window;
-  // stream mode launches one persistent wave per SIMD slot of the variant's
-  // bf16 kernel; the f32 sliding kernel fits one wave per SIMD, so it launches
-  // half as many (one round, the slots it leaves unused stay in the workspace)
+  // stream and group modes launch one persistent wave per SIMD slot of the
+  // variant's bf16 kernel; the f32 sliding kernel fits one wave per SIMD, so
+  // it launches half as many (one round, the slots it leaves unused stay in
+  // the workspace)
   const int launch_waves =
       !unit_mode && variant == GQA_SLIDING && !bf16 ? plan.waves / 2 : plan.waves;
   ka.n_waves = launch_waves;
   ka.ring = ring;
 
-  MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(unit_mode, paged, bf16)
-                   : kfv                   ? pick_main<4, 512, true>(unit_mode, paged, bf16)
-                                           : pick_main<4, 512, false>(unit_mode, paged, bf16);
+  MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(plan.mode, paged, bf16)
+                   : kfv                   ? pick_main<4, 512, true>(plan.mode, paged, bf16)
+                                           : pick_main<4, 512, false>(plan.mode, paged, bf16);
   ProfRec* pr = prof_slot(kfv ? kProfKeysFromValues : 2 * variant);
   if (pr) (void)hipEventRecord(pr->start, stream);
   hipLaunchKernelGGL(main_fn, dim3((unsigned)(launch_waves / kWaves)), dim3(kThreads), 0, stream,
@@ -1569,7 +1733,8 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ca.ws_acc = ka.ws_acc;
   ca.o = ka.o;
   ca.B = B;
-  ca.n_waves = launch_waves;
+  ca.n_waves = group_mode ? launch_waves / kWaves : launch_waves;
+  ca.groups = group_mode ? 1 : 0;
   const int ds = variant == GQA_SLIDING ? combine_parts<256>(B) : combine_parts<512>(B);
   const int cw = combine_waves(B * kHeads * ds);
   CombineFn comb =
@@ -1878,6 +2043,12 @@ const char* gqa_status_str(int32_t status) {
     case GQA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+int gqa_decode_force_mode(int32_t mode) {
+  if (mode < -1 || mode > GQA_MODE_GROUP) return GQA_ERR_SHAPE;
+  g_force_mode = mode;
+  return GQA_OK;
 }
 
 int gqa_hbm_read_probe(const void* src, size_t bytes, void* sink, void* stream) {

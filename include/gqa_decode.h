@@ -315,7 +315,7 @@ int gqa_decode_global_paged_noalloc(const void* q, const void* k_pool, const voi
 size_t gqa_decode_workspace_bytes(int32_t variant, int32_t B, int32_t capacity);
 
 /* launch modes reported by gqa_decode_plan */
-enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1 };
+enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1, GQA_MODE_GROUP = 2 };
 
 /* The launch plan for these arguments (a function of them alone).
  * GQA_MODE_UNIT: one work-group of four waves per (sequence, kv head), used
@@ -326,6 +326,10 @@ enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1 };
  * GQA_MODE_STREAM: *n_waves persistent waves each take an equal share of all
  *   tiles, partials of units shared by several waves go to *n_slots workspace
  *   slots, and a combine kernel merges them.
+ * GQA_MODE_GROUP: *n_waves / 4 work-groups each take an equal share of all
+ *   tiles (their four waves share each unit piece and merge it in LDS);
+ *   partials of units shared by several work-groups go to *n_slots workspace
+ *   slots, and the combine kernel merges them.
  * Returns GQA_OK or GQA_ERR_SHAPE / GQA_ERR_DTYPE. */
 int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* mode,
                     int32_t* n_waves, int32_t* n_slots);
@@ -337,6 +341,12 @@ int gqa_decode_constants(int32_t variant, int32_t* heads, int32_t* kv_heads, int
 
 /* Static description of a status code. */
 const char* gqa_status_str(int32_t status);
+
+/* Measurement and test utility: every later plan (and call) takes launch mode
+ * `mode` (GQA_MODE_*) whatever the planner would choose, or the planner's
+ * choice again for mode = -1.  Process-wide and not thread-safe; each mode
+ * computes the same attention.  Returns GQA_OK or GQA_ERR_SHAPE. */
+int gqa_decode_force_mode(int32_t mode);
 
 /* Measurement utilities, not part of the attention path: a plain read stream
  * of `bytes` bytes from `src` (non-temporal 16-byte loads, 1 KiB contiguous

@@ -43,11 +43,11 @@ static void plans(void) {
                           B <= 256 && cap >= 1 && cap <= 262144;
         if (valid) {
           expect("plan of a valid shape", st, GQA_OK);
-          if (mode != GQA_MODE_UNIT && mode != GQA_MODE_STREAM) {
+          if (mode != GQA_MODE_UNIT && mode != GQA_MODE_STREAM && mode != GQA_MODE_GROUP) {
             fprintf(stderr, "FAIL plan mode %d (variant %d B %d cap %d)\n", mode, variant, B, cap);
             ++failures;
           }
-          if (waves < 1 || slots < 0 || (mode == GQA_MODE_STREAM && ws == 0)) {
+          if (waves < 1 || slots < 0 || (mode != GQA_MODE_UNIT && ws == 0)) {
             fprintf(stderr, "FAIL plan waves %d slots %d ws %zu (variant %d B %d cap %d)\n", waves,
                     slots, ws, variant, B, cap);
             ++failures;

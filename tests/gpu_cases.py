@@ -10,6 +10,9 @@ import oracle
 import synth
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}  # max-abs error bars for unit-RMS values
+# the planner's mode for units split across slices: wave slices (stream) on the
+# sliding geometry, work-group slices (group) on the global one
+SPLIT_MODE = {"sliding": "stream", "global": "group"}
 
 
 def hip_run(case: synth.Case, workspace=None, stream=None, o=None, window=None) -> torch.Tensor:

@@ -72,16 +72,19 @@ def test_plan_and_workspace(lib, variant, B, cap):
         assert plan == {"mode": "unit", "waves": 4 * B * KV, "slots": 0}
         assert ws == 0
     else:
-        assert plan["mode"] == "stream"
+        # split units: wave slices (stream mode) on the sliding geometry, work-group
+        # slices (group mode) on the global one; slot u + w for every (unit, slice)
+        assert plan["mode"] == ("stream" if variant == "sliding" else "group")
         assert plan["waves"] == (2048 if variant == "sliding" else 1024)
-        assert plan["slots"] == B * KV + plan["waves"]   # slot u + w for every (unit, wave)
+        slices = plan["waves"] if variant == "sliding" else plan["waves"] // 4
+        assert plan["slots"] == B * KV + slices
         assert ws >= (B + 1) * 4 + plan["slots"] * G * (D + 2) * 4
 
 
 def test_plan_modes_of_the_workloads(lib):
     assert gqa.gqa_decode_plan("sliding", 256, 8192)["mode"] == "unit"
-    assert gqa.gqa_decode_plan("global", 32, 131072)["mode"] == "stream"
-    assert gqa.gqa_decode_plan("global", 1, 262144)["mode"] == "stream"
+    assert gqa.gqa_decode_plan("global", 32, 131072)["mode"] == "group"
+    assert gqa.gqa_decode_plan("global", 1, 262144)["mode"] == "group"
     assert gqa.gqa_decode_plan("sliding", 4, 2048)["mode"] == "stream"
 
 

@@ -27,8 +27,8 @@ SHAPES = {
     "sliding-f32-stream": ("sliding", "f32", 4, 2048, False, None, False, "stream"),
     "window-stream": ("sliding", "bf16", 4, 9008, True, 4096, False, "stream"),
     "global-unit": ("global", "bf16", 256, 512, False, None, False, "unit"),
-    "global-stream-paged": ("global", "bf16", 3, 16384, True, None, False, "stream"),
-    "values-only-stream": ("global", "bf16", 3, 16384, True, None, True, "stream"),
+    "global-group-paged": ("global", "bf16", 3, 16384, True, None, False, "group"),
+    "values-only-group": ("global", "bf16", 3, 16384, True, None, True, "group"),
 }
 
 
@@ -83,7 +83,7 @@ def test_graph_replay_equals_eager(key):
 def test_graph_of_several_calls():
     # a sliding and a global call, each twice, in one graph (the second of
     # each pair reuses the first's workspace)
-    parts = [_case("sliding-stream-paged", 950), _case("global-stream-paged", 951)]
+    parts = [_case("sliding-stream-paged", 950), _case("global-group-paged", 951)]
     refs = []
     for _, call, o, _ in parts:
         call()

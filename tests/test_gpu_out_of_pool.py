@@ -78,8 +78,8 @@ BAD_IDS = lambda num_pages: (num_pages, num_pages + 1000, -1, -7)  # noqa: E731
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("B,cap,mode", [(3, 4096, "stream"), (64, 512, "unit")],
-                         ids=["stream", "unit"])
+@pytest.mark.parametrize("B,cap,mode", [(3, 4096, "group"), (64, 512, "unit")],
+                         ids=["group", "unit"])
 def test_decode_global_drops_out_of_pool_pages(B, cap, mode, dtype):
     assert gqa.gqa_decode_plan("global", B, cap)["mode"] == mode
     lens = synth.draw_seq_lens(("uniform", 40, cap), B, 51).tolist()

@@ -10,7 +10,7 @@ import torch
 import decode_attention_slidingdecodegqa_amd as gqa
 import oracle_pins
 import synth
-from gpu_cases import TOL, hip_run, max_err, oracle_run, to_f64, to_gpu
+from gpu_cases import SPLIT_MODE, TOL, hip_run, max_err, oracle_run, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -57,14 +57,15 @@ def test_parity_batch_shapes(variant):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("variant", ["sliding", "global"])
 def test_combine_d_parts(variant, dtype):
-    # stream mode at batch sizes that give the combine 8, 4, 2 and 1 d parts per head
+    # split units (stream mode, group mode on the global geometry) at batch
+    # sizes that give the combine 8, 4, 2 and 1 d parts per head
     # (fewer than 256 (sequence, head) rows split each head's D across work-groups)
     # and work-groups of eight and of four waves (above 512 groups); sliding with a
     # 2048 window, whose 129-tile units keep these batches in stream mode
     cap = SMALL[variant][0]
     window = 2048 if variant == "sliding" else None
     for B in ((1, 2, 5, 16, 24, 31, 33) if dtype == "bf16" else (1, 16, 33)):
-        assert gqa.gqa_decode_plan(variant, B, cap, window=window)["mode"] == "stream"
+        assert gqa.gqa_decode_plan(variant, B, cap, window=window)["mode"] == SPLIT_MODE[variant]
         lens = synth.draw_seq_lens(("uniform", 1, cap), B, 200 + B)
         lens[0] = cap
         c = synth.make_case(variant, dtype, B, cap, lens, seed=200 + B, window=window)
@@ -111,9 +112,10 @@ def stream_waves(variant, dtype, plan_waves, T):
 
 
 def slice_boundary_positions(variant, lens, cap, dtype="bf16"):
-    """For each sequence, the first position of a tile that starts a new wave
-    slice inside kv head 0's unit (the position where two slices of the
-    stream partition meet), or the unit's middle if one slice holds it."""
+    """For each sequence, the first position of a tile that starts a new slice
+    inside kv head 0's unit (where two wave slices of the stream partition, or
+    two work-group slices of the group partition, meet), or the unit's middle
+    if one slice holds it."""
     KV = 16 if variant == "sliding" else 4
     plan = gqa.gqa_decode_plan(variant, len(lens), cap)
     rng = []
@@ -123,7 +125,14 @@ def slice_boundary_positions(variant, lens, cap, dtype="bf16"):
         t0 = lo // 16
         rng.append((lo, L, t0, (L + 15) // 16 - t0))
     T = KV * sum(n for *_, n in rng)
-    W = stream_waves(variant, dtype, plan["waves"], T) if plan["mode"] == "stream" else 1
+    if plan["mode"] == "stream":
+        W = stream_waves(variant, dtype, plan["waves"], T)
+    elif plan["mode"] == "group":
+        # work-groups: the launch's, or one per 4 tiles when that is fewer
+        groups = plan["waves"] // 4
+        W = min(groups, max(1, -(-T // 4)))
+    else:
+        W = 1
     out, first = [], 0
     for lo, L, t0, n in rng:
         s0 = first                       # flattened first tile of unit (b, g=0)
@@ -250,7 +259,7 @@ def test_side_stream_without_entering_it(variant):
     # side stream's kernels from being reused before they complete.
     cap = 4096
     c = to_gpu(synth.make_case(variant, "bf16", 4, cap, [4096, 5, 3000, 1], seed=115))
-    assert gqa.gqa_decode_plan(variant, 4, cap)["mode"] == "stream"
+    assert gqa.gqa_decode_plan(variant, 4, cap)["mode"] == SPLIT_MODE[variant]
     need = gqa.gqa_decode_workspace_bytes(variant, 4, cap)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -13,8 +13,9 @@ stress_cases.py) that
     between 0 and 1 in every wave, and partials whose maxima differ widely;
   * are large and random (about +-100 bf16, +-25 f32; the values-only
     calls within their accuracy envelope, tests/stress_cases.py).
-They run in both launch modes (unit: one work-group per (sequence, kv head);
-stream: units split across waves, merged by the combine kernel), both cache
+They run in the planner's launch modes (unit: one work-group per (sequence,
+kv head); stream on the sliding geometry and group on the global one: units
+split across waves or work-groups, merged by the combine kernel), both cache
 forms, f32 and bf16, for the decode, runtime-window, values-only and prefill
 calls.  The bars are the usual 1e-4 (f32) and 2e-2 (bf16) max-abs errors.
 """
@@ -44,7 +45,7 @@ DECODE_SHAPES = {
     "sliding-stream": ("sliding", None, 4, 4096, [4096, 1025, 3000, 17], "stream"),
     "window4096-stream": ("sliding", 4096, 4, 9008, [9008, 4097, 2500, 6000], "stream"),
     "global-unit": ("global", None, 64, 512, None, "unit"),
-    "global-stream": ("global", None, 3, 16384, [16384, 9000, 333], "stream"),
+    "global-group": ("global", None, 3, 16384, [16384, 9000, 333], "group"),
 }
 
 
@@ -74,7 +75,7 @@ def test_decode_softmax_stress(shape, pattern, dtype, paged):
 
 @pytest.mark.parametrize("paged", [False, True], ids=["contig", "paged"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("B,cap", [(64, 512), (3, 16384)], ids=["unit", "stream"])
+@pytest.mark.parametrize("B,cap", [(64, 512), (3, 16384)], ids=["unit", "group"])
 def test_values_only_large_logits(B, cap, dtype, paged):
     # keys rebuilt from values: the query alone carries the scale (the values
     # are the keys, so scaling them would scale the outputs too), within the

@@ -39,7 +39,7 @@ def test_noalloc_matches_the_workspace_entry_point(dtype):
     small = to_gpu(synth.make_case("global", dtype, 3, 2048, [2048, 700, 1], paged=True,
                                    seed=502, extra_pages=2))
     for c in (big, small):
-        assert gqa.gqa_decode_plan("global", c.B, c.cap)["mode"] == "stream"
+        assert gqa.gqa_decode_plan("global", c.B, c.cap)["mode"] == "group"
     got_big = _noalloc(big)
     got_small = _noalloc(small)          # the second call, on a smaller input
     torch.cuda.synchronize()
