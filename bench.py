@@ -427,7 +427,7 @@ def section_step(ctx, line):
     achieved = gl_bytes / (gl_main * 1e-6) / 1e9
     trace_us, trace_box, trace_current = read_trace("global_main")
     line["roofline"] = {
-        "kernel": "gqa_stream_kernel<4,512,paged,bf16> (decodeGQA, B=32 paged)",
+        "kernel": "gqa_group_kernel<4,512,paged,bf16> (decodeGQA, B=32 paged, group mode)",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
         "kernel_us": round(gl_main, 2), "box": box_name(),
