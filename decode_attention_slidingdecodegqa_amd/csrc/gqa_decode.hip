@@ -802,24 +802,33 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   }
 }
 
-// The four waves' states of one unit merged through LDS: waves 1..3 write
-// their O rows and (m, l), and wave 0's lanes r < G fold them into their own
-// state in place (st.m becomes the common reference max, Lt the total
-// weight).  Returns true on those lanes, which alone hold the merged state.
-// Every wave of the work-group calls it (it holds a barrier); s_acc holds
-// 3 G rows of D + 4 floats, s_m and s_l 3 G floats.
+// The four waves' states of one unit (or unit piece) merged through LDS and
+// written by all four waves, each a quarter of D: every wave stores its O rows
+// and (m, l) (lanes r < G), then wave w folds the four rows on
+// d in [wD/4, (w+1)D/4) with the common reference max.  Lane l of wave w takes
+// the PER = G*D/256 consecutive values e0 = PER*l of that quarter's G x D/4
+// block (head e0 / (D/4)).  Writes either o (whole unit: the merged row over
+// the total weight, in the output dtype) or the unnormalised fp32 partial row
+// and its (m, l) (the lane starting a head's quarter 0 writes the pair).
+// s_acc holds 4 G rows of D + 4 floats, s_m and s_l 4 G floats; every wave of
+// the work-group calls it (it holds a barrier, and a second one before the
+// LDS rows may be reused).
 template <int KV, int D, bool BF16>
-__device__ __forceinline__ bool merge_group(WaveState<KV, D, BF16>& st, float* s_acc, float* s_m,
-                                            float* s_l, float& Lt) {
+__device__ __forceinline__ void merge_store_group(const WaveState<KV, D, BF16>& st, float* s_acc,
+                                                  float* s_m, float* s_l, char* o_unit,
+                                                  float* ws_acc_slot, float* ws_ml_slot) {
   using Gm = Geo<KV, D, BF16>;
-  constexpr int G = Gm::G, E = Gm::E, VBLK = Gm::VBLK;
+  constexpr int G = Gm::G, E = Gm::E, VBLK = Gm::VBLK, EB = Gm::EB;
   constexpr int LROW = D + 4;  // padded LDS row (floats)
+  constexpr int Q = D / kWaves;            // d values per wave
+  constexpr int PER = G * Q / 64;          // values per lane
+  static_assert(PER == 2 || PER % 4 == 0, "merge width");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;
   const int j = lane >> 4;
-  if (wave > 0 && r < G) {
-    float* dst = s_acc + ((wave - 1) * G + r) * LROW;
+  if (r < G) {
+    float* dst = s_acc + (wave * G + r) * LROW;
 #pragma unroll
     for (int blk = 0; blk < VBLK; ++blk)
 #pragma unroll
@@ -827,45 +836,69 @@ __device__ __forceinline__ bool merge_group(WaveState<KV, D, BF16>& st, float* s
 #pragma unroll
         for (int e = 0; e < E; ++e) dst[16 * E * blk + 4 * E * j + E * i + e] = st.acc[blk][e][i];
     if (j == 0) {
-      s_m[(wave - 1) * G + r] = st.m;
-      s_l[(wave - 1) * G + r] = st.l;
+      s_m[wave * G + r] = st.m;
+      s_l[wave * G + r] = st.l;
     }
   }
   __syncthreads();
-  if (wave != 0 || r >= G) return false;
-
-  float M = st.m;
-  float mw[kWaves - 1], lw[kWaves - 1];
+  const int e0 = PER * lane;
+  const int h = e0 / Q;
+  const int d = wave * Q + e0 % Q;
+  float M = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < kWaves - 1; ++v) {
-    mw[v] = s_m[v * G + r];
-    lw[v] = s_l[v * G + r];
-    M = fmaxf(M, mw[v]);
-  }
+  for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v * G + h]);
   const float Muse = M == -INFINITY ? 0.f : M;
-  const float sc0 = exp2_fast((st.m - Muse) * kLog2e);
-  float sc[kWaves - 1];
-  Lt = sc0 * st.l;
+  float sc[kWaves];
+  float Lt = 0.f;
 #pragma unroll
-  for (int v = 0; v < kWaves - 1; ++v) {
-    sc[v] = exp2_fast((mw[v] - Muse) * kLog2e);
-    Lt += sc[v] * lw[v];
+  for (int v = 0; v < kWaves; ++v) {
+    sc[v] = exp2_fast((s_m[v * G + h] - Muse) * kLog2e);
+    Lt += sc[v] * s_l[v * G + h];
   }
+  float x[PER];
 #pragma unroll
-  for (int blk = 0; blk < VBLK; ++blk)
+  for (int k = 0; k < PER; ++k) x[k] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      f32x4 x = sc0 * st.acc[blk][e];
+  for (int v = 0; v < kWaves; ++v) {
+    const float* row = s_acc + (v * G + h) * LROW + d;
 #pragma unroll
-      for (int v = 0; v < kWaves - 1; ++v) {
-        const float* row = s_acc + (v * G + r) * LROW + 16 * E * blk + 4 * E * j + e;
-        x += sc[v] * f32x4{row[0], row[E], row[2 * E], row[3 * E]};
+    for (int k = 0; k < PER; ++k) x[k] += sc[v] * row[k];
+  }
+  if (o_unit != nullptr) {
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    char* dst = o_unit + ((size_t)h * D + d) * EB;
+    if constexpr (BF16) {
+      if constexpr (PER == 2) {
+        *reinterpret_cast<unsigned*>(dst) = bf16_pack2(x[0] * inv, x[1] * inv);
+      } else {
+#pragma unroll
+        for (int c = 0; c < PER / 4; ++c)
+          *reinterpret_cast<u32x2*>(dst + 8 * c) =
+              u32x2{bf16_pack2(x[4 * c] * inv, x[4 * c + 1] * inv),
+                    bf16_pack2(x[4 * c + 2] * inv, x[4 * c + 3] * inv)};
       }
-      st.acc[blk][e] = x;
+    } else {
+      if constexpr (PER == 2) {
+        *reinterpret_cast<f32x2*>(dst) = f32x2{x[0] * inv, x[1] * inv};
+      } else {
+#pragma unroll
+        for (int c = 0; c < PER / 4; ++c)
+          *reinterpret_cast<f32x4*>(dst + 16 * c) =
+              f32x4{x[4 * c] * inv, x[4 * c + 1] * inv, x[4 * c + 2] * inv, x[4 * c + 3] * inv};
+      }
     }
-  st.m = M;
-  st.l = Lt;
-  return true;
+  } else {
+    float* dst = ws_acc_slot + (size_t)h * D + d;
+    if constexpr (PER == 2) {
+      *reinterpret_cast<f32x2*>(dst) = f32x2{x[0], x[1]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < PER / 4; ++c)
+        *reinterpret_cast<f32x4*>(dst + 4 * c) = f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
+    }
+    if (wave == 0 && e0 % Q == 0) *reinterpret_cast<f32x2*>(ws_ml_slot + 2 * h) = f32x2{M, Lt};
+  }
+  __syncthreads();  // the rows are read before anyone reuses the LDS
 }
 
 // ---- unit kernel: one work-group per unit (many short units); its four
@@ -877,15 +910,15 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   constexpr int G = Gm::G, ROW = Gm::ROW, NCH = Gm::NCH;
   constexpr int LROW = D + 4;  // padded LDS row (floats)
   __shared__ u32x4 s_q[kWaves][G * NCH];
-  // the merge rows of waves 1..3; the staged path's per-wave tiles share the
+  // the merge rows of the four waves; the staged path's per-wave tiles share the
   // space (every wave has left its tile loop before the merge writes)
   constexpr int SB = wave_stage_bytes<KFV, BF16, ROW>();  // per wave
-  constexpr int ACC_BYTES = (kWaves - 1) * G * LROW * 4;
+  constexpr int ACC_BYTES = kWaves * G * LROW * 4;
   constexpr int POOL = kWaves * SB > ACC_BYTES ? kWaves * SB : ACC_BYTES;
   __shared__ __attribute__((aligned(16))) char s_pool[POOL];
   float* s_acc = reinterpret_cast<float*>(s_pool);
-  __shared__ float s_m[(kWaves - 1) * G];
-  __shared__ float s_l[(kWaves - 1) * G];
+  __shared__ float s_m[kWaves * G];
+  __shared__ float s_l[kWaves * G];
   __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
   RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
   if constexpr (KFV) {
@@ -911,10 +944,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
                                             SB > 0 ? s_pool + wave * SB : nullptr, st);
   if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
 
-  float Lt;
-  if (!merge_group<KV, D, BF16>(st, s_acc, s_m, s_l, Lt)) return;
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  store_o<KV, D, BF16>(st, a.o + ((size_t)b * kHeads + g * G + r) * ROW, inv);
+  merge_store_group<KV, D, BF16>(st, s_acc, s_m, s_l, a.o + ((size_t)b * kHeads + g * G) * ROW,
+                                 nullptr, nullptr);
 }
 
 // ---- group kernel: the stream partition over work-groups
@@ -951,16 +982,16 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   __shared__ int s_cnt[kMaxBatch];
   __shared__ int s_before[kMaxBatch + 1];
   __shared__ u32x4 s_q[kWaves][G * NCH];
-  // the per-wave tiles and the merge rows of waves 1..3 share the space (the
+  // the per-wave tiles and the merge rows of the four waves share the space (the
   // tile loops of a piece end before its merge writes, and a barrier ends
   // the merge before the next piece's tiles)
   constexpr int SB = wave_stage_bytes<KFV, BF16, ROW>();  // per wave
-  constexpr int ACC_BYTES = (kWaves - 1) * G * LROW * 4;
+  constexpr int ACC_BYTES = kWaves * G * LROW * 4;
   constexpr int POOL = kWaves * SB > ACC_BYTES ? kWaves * SB : ACC_BYTES;
   __shared__ __attribute__((aligned(16))) char s_pool[POOL];
   float* s_acc = reinterpret_cast<float*>(s_pool);
-  __shared__ float s_m[(kWaves - 1) * G];
-  __shared__ float s_l[(kWaves - 1) * G];
+  __shared__ float s_m[kWaves * G];
+  __shared__ float s_l[kWaves * G];
   __shared__ std::conditional_t<KFV, RopeLds, int> s_rope_buf;
   RopeLds* s_rope = KFV ? reinterpret_cast<RopeLds*>(&s_rope_buf) : nullptr;
   if constexpr (KFV) rope_tables_init<BF16>(a.w_k, s_rope);
@@ -1005,18 +1036,13 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
                                               s_q[wave], s_rope,
                                               SB > 0 ? s_pool + wave * SB : nullptr, st);
     if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
-    float Lt;
-    const bool holder = merge_group<KV, D, BF16>(st, s_acc, s_m, s_l, Lt);
-    const int unit = b * KV + g;
-    if (k_begin == 0 && k_end == n) {
-      if (holder) store_o<KV, D, BF16>(st, a.o + ((size_t)b * kHeads + g * G + r) * ROW,
-                                       Lt > 0.f ? 1.f / Lt : 0.f);
-    } else if (holder) {
-      const size_t slot = (size_t)unit + grp;
-      store_partial<KV, D, BF16>(st, a.ws_acc + (slot * G + r) * D);
-      if (j == 0) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + r) * 2) = f32x2{st.m, Lt};
-    }
-    __syncthreads();  // the merge rows are reused by the next piece
+    // a whole unit writes o; a piece writes the work-group's partial to slot
+    // unit + grp (the merge ends on a barrier: its LDS rows may then be reused)
+    const size_t slot = (size_t)(b * KV + g) + grp;
+    merge_store_group<KV, D, BF16>(
+        st, s_acc, s_m, s_l,
+        k_begin == 0 && k_end == n ? a.o + ((size_t)b * kHeads + g * G) * ROW : nullptr,
+        a.ws_acc + slot * G * D, a.ws_ml + slot * G * 2);
 
     // ---- next unit (skipping sequences with nothing attended)
     t += k_end - k_begin;
