@@ -21,8 +21,9 @@ namespace {
 // double-buffered LDS tile with padded rows (operand reads free of bank
 // conflicts, every operand address a lane base plus an immediate), which all
 // waves use with every MFMA column masked to its own range.  bf16 P@V runs on 16x16x32 MFMAs over both halves
-// of a step.  Work-groups of one (b, g) are placed on one XCD so their shared
-// tiles stay in that XCD's L2.
+// of a step.  Under a windowed mask, work-groups of one (b, g) are placed on
+// one XCD so their shared tiles stay in that XCD's L2; under the full causal
+// mask they are dealt longest first over all XCDs.
 
 struct PrefillArgs {
   const char* q;
@@ -153,11 +154,31 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     if (lane == 63) s_wg0[a.B] = incl;
   }
   __syncthreads();
-  // XCD-aware order: the hardware deals work-groups round-robin over the XCDs,
-  // so consecutive logical work-groups (same (b, g), neighbouring columns)
-  // are given block ids that land on one XCD (gridDim.x is a multiple of 8)
-  const int wg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
-  if (wg >= s_wg0[a.B]) return;  // the whole work-group leaves together
+  // Block id -> logical work-group.  The hardware deals block ids round-robin
+  // over the XCDs (gridDim.x is a multiple of 8, so block x runs on XCD x % 8)
+  // and each XCD starts its blocks in id order.  The host sizes the grid from
+  // an upper bound; the true count nwg is only known here, and the mapping
+  // spreads that count, not the bound, over the XCDs (an XCD given a larger
+  // share finishes last and the others idle).
+  // - windowed mask: work-groups of one (b, g) with neighbouring columns share
+  //   most of their keys, so XCD x takes a contiguous range of about nwg/8 of
+  //   them and keeps the shared tiles in its own L2;
+  // - full causal mask: a later column block attends to more keys, so the
+  //   blocks are dealt longest first (block id 0 takes the last work-group)
+  //   and round-robin over the XCDs, which balances the XCDs' work and lets
+  //   the last blocks started be the shortest.  Every work-group of a (b, g)
+  //   reads that sequence's keys from position 0, so the L2s still share them.
+  const int nwg = s_wg0[a.B];
+  int wg;
+  if (a.window > 0) {
+    const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
+    const int lo = xcd * nwg / kXcds, hi = (xcd + 1) * nwg / kXcds;
+    if (slot >= hi - lo) return;  // the whole work-group leaves together
+    wg = lo + slot;
+  } else {
+    if ((int)blockIdx.x >= nwg) return;
+    wg = nwg - 1 - (int)blockIdx.x;
+  }
   int b = 0;
   {
     int lo_b = 0, hi_b = a.B - 1;
