@@ -3,6 +3,9 @@
 // with the causal and sliding masks of the architecture page's compact
 // forward pass).  The C ABI is declared in include/gqa_decode.h.
 
+#include <algorithm>
+#include <atomic>
+
 #include "gqa_common.h"
 
 namespace {
@@ -23,7 +26,8 @@ namespace {
 // waves use with every MFMA column masked to its own range.  bf16 P@V runs on 16x16x32 MFMAs over both halves
 // of a step.  Under a windowed mask, work-groups of one (b, g) are placed on
 // one XCD so their shared tiles stay in that XCD's L2; under the full causal
-// mask they are dealt longest first over all XCDs.
+// mask they are dealt longest first over all XCDs.  bf16 sliding blocks are
+// persistent, one per CU, each taking a list of work-groups.
 
 struct PrefillArgs {
   const char* q;
@@ -76,7 +80,9 @@ constexpr int prefill_cols_per_wg() {
   return 16 * prefill_col_blocks<KV, BF16>() * prefill_waves<KV, BF16>();
 }
 
-template <int KV, int D, bool PAGED, bool BF16>
+// PERSIST: the block takes a list of items (the grid is sized from the CU
+// count); otherwise one item per block.
+template <int KV, int D, bool PAGED, bool BF16, bool PERSIST>
 __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_per_simd<KV, BF16>())) void gqa_prefill_kernel(
     PrefillArgs a) {
   using Gm = Geo<KV, D, BF16>;
@@ -109,7 +115,6 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
-  const int g = blockIdx.y;
 
   // ---- work-groups per sequence (ceil(T_b*G / 64)) and their prefix, in LDS
   __shared__ int s_wg0[kMaxBatch + 1];
@@ -154,31 +159,45 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
     if (lane == 63) s_wg0[a.B] = incl;
   }
   __syncthreads();
-  // Block id -> logical work-group.  The hardware deals block ids round-robin
-  // over the XCDs (gridDim.x is a multiple of 8, so block x runs on XCD x % 8)
-  // and each XCD starts its blocks in id order.  The host sizes the grid from
-  // an upper bound; the true count nwg is only known here, and the mapping
-  // spreads that count, not the bound, over the XCDs (an XCD given a larger
-  // share finishes last and the others idle).
-  // - windowed mask: work-groups of one (b, g) with neighbouring columns share
-  //   most of their keys, so XCD x takes a contiguous range of about nwg/8 of
-  //   them and keeps the shared tiles in its own L2;
+  // ---- the work-groups of the call, flattened kv head major (item f is
+  // work-group f % nwg of kv head f / nwg), and the block's items.  The
+  // hardware deals block ids round-robin over the XCDs (gridDim.x is a
+  // multiple of 8, so block x runs on XCD x % 8) and each XCD starts its
+  // blocks in id order.  The host sizes the grid from an upper bound of the
+  // items (one per block) or from the CU count (persistent blocks, each
+  // taking a list of items, which saves a block launch and the prefix of
+  // cu_q per item); the true count is only known here, and the map spreads
+  // that count, not the bound, over the XCDs (an XCD given a larger share
+  // finishes last while the others idle).
+  // - windowed mask: items of one (b, g) with neighbouring columns share most
+  //   of their keys, so XCD x takes a contiguous range of about 1/8 of them,
+  //   which its blocks take in turn (the items running together on an XCD are
+  //   neighbours and share the tiles in its L2; odd rounds take the slots in
+  //   reverse, which evens out a length trend);
   // - full causal mask: a later column block attends to more keys, so the
-  //   blocks are dealt longest first (block id 0 takes the last work-group)
-  //   and round-robin over the XCDs, which balances the XCDs' work and lets
-  //   the last blocks started be the shortest.  Every work-group of a (b, g)
-  //   reads that sequence's keys from position 0, so the L2s still share them.
-  const int nwg = s_wg0[a.B];
-  int wg;
-  if (a.window > 0) {
-    const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
-    const int lo = xcd * nwg / kXcds, hi = (xcd + 1) * nwg / kXcds;
-    if (slot >= hi - lo) return;  // the whole work-group leaves together
-    wg = lo + slot;
-  } else {
-    if ((int)blockIdx.x >= nwg) return;
-    wg = nwg - 1 - (int)blockIdx.x;
-  }
+  //   items are dealt longest first, round-robin over the XCDs, in rounds of
+  //   gridDim.x that alternate direction (a persistent block's items then
+  //   pair long with short).  Every item of a (b, g) reads that sequence's
+  //   keys from position 0, so the L2s still share them.
+  const int nwg = s_wg0[a.B];  // work-groups per kv head
+  const int total = KV * nwg;
+  auto item_at = [&](int k) -> int {
+    if (a.window > 0) {
+      const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
+      const int S = (int)(gridDim.x / kXcds);
+      const int lo = (int)((long)xcd * total / kXcds), hi = (int)((long)(xcd + 1) * total / kXcds);
+      const long f = (long)lo + (long)k * S + ((k & 1) ? S - 1 - slot : slot);
+      return f < hi ? (int)f : -1;
+    }
+    const long P = gridDim.x;
+    const long rank = (long)k * P + ((k & 1) ? P - 1 - (long)blockIdx.x : (long)blockIdx.x);
+    return rank < total ? (int)(total - 1 - rank) : -1;
+  };
+  for (int k = 0; k == 0 || PERSIST; ++k) {
+  const int f = item_at(k);
+  if (f < 0) break;  // the whole work-group leaves together
+  const int g = __builtin_amdgcn_readfirstlane(f / nwg);
+  const int wg = f % nwg;
   int b = 0;
   {
     int lo_b = 0, hi_b = a.B - 1;
@@ -647,15 +666,41 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
       }
     }
   }
+  }  // items
 }
 
 typedef void (*PrefillFn)(PrefillArgs);
 
+// bf16 sliding prefill blocks are persistent, one per CU (one work-group per
+// CU fits the registers and LDS).  The global layer's items are long (an
+// item's start is about 1% of one) and run one per block.
+template <int KV, bool BF16>
+constexpr bool prefill_persist() {
+  return BF16 && KV == 16;
+}
+
+// compute units of the current device (cached per device; 256 on MI355X)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < kXcds)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int KV, int D>
 PrefillFn pick_prefill(bool paged, bool bf16) {
   if (paged)
-    return bf16 ? gqa_prefill_kernel<KV, D, true, true> : gqa_prefill_kernel<KV, D, true, false>;
-  return bf16 ? gqa_prefill_kernel<KV, D, false, true> : gqa_prefill_kernel<KV, D, false, false>;
+    return bf16 ? gqa_prefill_kernel<KV, D, true, true, prefill_persist<KV, true>()>
+                : gqa_prefill_kernel<KV, D, true, false, false>;
+  return bf16 ? gqa_prefill_kernel<KV, D, false, true, prefill_persist<KV, true>()>
+              : gqa_prefill_kernel<KV, D, false, false, false>;
 }
 
 constexpr int kMaxPrefillRows = 1 << 24;  // query rows per call
@@ -700,20 +745,27 @@ int run_prefill(int variant, bool paged, const void* q, const void* k, const voi
   const bool bf16 = dtype == GQA_BF16;
   PrefillFn fn = variant == GQA_SLIDING ? pick_prefill<16, 256>(paged, bf16)
                                         : pick_prefill<4, 512>(paged, bf16);
-  // an upper bound of the work-groups sum_b ceil(T_b*G/64): the rest exit at once
+  // an upper bound of the items, KV * sum_b ceil(T_b*G/CPW) (the kernel finds
+  // the true count; blocks without an item leave at once), or persistent
+  // blocks, one per CU, each taking a list of items.  The kernel's XCD map
+  // needs a multiple of 8 blocks.
   const int G = kHeads / vi.KV;
   const int cpw = variant == GQA_SLIDING
                       ? (bf16 ? prefill_cols_per_wg<16, true>() : prefill_cols_per_wg<16, false>())
                       : (bf16 ? prefill_cols_per_wg<4, true>() : prefill_cols_per_wg<4, false>());
-  int64_t n_wg = ((int64_t)N * G + cpw - 1) / cpw + B;
-  n_wg = (n_wg + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD remap needs a multiple of 8
-  const unsigned grid_x = (unsigned)n_wg;
+  int64_t n_items = (((int64_t)N * G + cpw - 1) / cpw + B) * vi.KV;
+  const bool persist = variant == GQA_SLIDING
+                           ? (bf16 ? prefill_persist<16, true>() : prefill_persist<16, false>())
+                           : (bf16 ? prefill_persist<4, true>() : prefill_persist<4, false>());
+  if (persist) n_items = std::min<int64_t>(n_items, device_cus() / kXcds * kXcds);
+  n_items = (n_items + kXcds - 1) / kXcds * kXcds;
+  const unsigned grid_x = (unsigned)n_items;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const int slot = gqa_detail::prof_begin(kProfPrefill + variant, stream);
   const unsigned threads = 64u * (unsigned)(variant == GQA_SLIDING
                                                 ? (bf16 ? prefill_waves<16, true>() : prefill_waves<16, false>())
                                                 : (bf16 ? prefill_waves<4, true>() : prefill_waves<4, false>()));
-  hipLaunchKernelGGL(fn, dim3(grid_x, (unsigned)vi.KV), dim3(threads), 0, stream, pa);
+  hipLaunchKernelGGL(fn, dim3(grid_x), dim3(threads), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   gqa_detail::prof_end(slot, stream);
   return GQA_OK;

@@ -155,6 +155,31 @@ def test_prefill_many_sequences(variant):
             assert max_err(got[cu[b] + n, h], ref[i]) <= TOL["bf16"], (b, n, h)
 
 
+def test_prefill_many_items_per_block_all_rows():
+    # more work-groups than CUs, so each persistent block of the bf16 sliding
+    # kernel takes a list of them: 96 sequences of 0..24 new tokens after pasts
+    # of 0..200 positions, a few with chunks longer than the sequence (their
+    # rows before position 0 are zero, some whole work-groups of them); every
+    # row vs the oracle, for both geometries (the global layer as a control)
+    g = torch.Generator().manual_seed(509)
+    B, cap = 96, 240
+    q_lens = torch.randint(0, 25, (B,), generator=g)
+    past = torch.randint(0, 201, (B,), generator=g)
+    lens = (past + q_lens).clamp(max=cap)
+    for b in (3, 40, 77):  # the chunk reaches before position 0 (b = 40: all of it)
+        q_lens[b] = 24
+        lens[b] = 0 if b == 40 else 5 + b % 7
+    for variant in ("sliding", "global"):
+        c = synth.make_prefill_case(variant, "bf16", cap, lens.tolist(), q_lens.tolist(), seed=509)
+        got = to_f64(hip_prefill(to_gpu(c)))
+        ref = oracle_prefill(c)
+        assert max_err(got, ref) <= TOL["bf16"], variant
+        cu = c.cu_q.tolist()
+        for b in (3, 40, 77):
+            before = q_lens[b].item() - lens[b].item()
+            assert not got[cu[b]:cu[b] + before].any(), (variant, b)
+
+
 def test_prefill_chunk_longer_than_sequence():
     # outside the domain: rows before position 0 are zero, the rest as defined
     c = synth.make_prefill_case("sliding", "bf16", 64, [5, 30], [8, 10], seed=506, fill=0.0)
