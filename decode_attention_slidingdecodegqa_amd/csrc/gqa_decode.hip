@@ -61,6 +61,8 @@ struct KernelArgs {
   int32_t window;
   int32_t n_waves;
   int32_t ring;  // > 0: contiguous cache capped at `ring` positions, position s in slot s % ring
+  int32_t* counter;  // group mode with a dynamic tail: the chunk counter (zero at launch)
+  int32_t dyn;       // nonzero: group mode may take a dynamic tail (tail_plan)
 };
 
 // Capacity that bounds a sequence's positions: the cache's, or for a ring
@@ -89,6 +91,36 @@ __device__ inline SeqRange seq_range(int L_raw, int cap, int window) {
 // Wave whose slice holds flattened tile t: slice w is [w*T/W, (w+1)*T/W).
 __device__ inline int wave_of(long t, long T, int W) {
   return (int)(((t + 1) * W - 1) / T);
+}
+
+// Dynamic tail of the group partition.  Equal static slices leave the XCDs
+// that read HBM faster idle at the end (measured per work-group on the global
+// B=32 step: four XCDs finished their slices in 2.53-2.57 ms, the other four
+// in 2.77-2.84 ms).  So in a large group-mode call the static slices cover the
+// first S tiles only, and the last ~1/12 of the tiles form nch chunks of C
+// tiles that the work-groups take from a counter when their slice is done.
+// Chunk c is slice W + c for the partial slots and the combine.
+constexpr long kDynMinTiles = 1L << 19;  // smaller calls (under ~2048 tiles per
+                                         // work-group): static slices only, a
+                                         // chunk there would be a large share
+constexpr int kDynMaxChunks = 768;    // partial slots a call may add
+constexpr int kDynMinChunk = 128;     // tiles per chunk at least
+struct TailPlan {
+  long S;   // tiles of the static slices
+  int C;    // tiles per chunk
+  int nch;  // chunks
+};
+__host__ __device__ inline TailPlan tail_plan(long T, int dyn) {
+  if (!dyn || T < kDynMinTiles) return TailPlan{T, 1, 0};
+  const long Td = T / 12;
+  long C = (Td + kDynMaxChunks - 1) / kDynMaxChunks;
+  if (C < kDynMinChunk) C = kDynMinChunk;
+  const int nch = (int)(Td / C);
+  return TailPlan{T - (long)nch * C, (int)C, nch};
+}
+// the slice holding flattened tile t (W static slices over [0, S), then the chunks)
+__device__ inline int slice_of(long t, const TailPlan& tp, int W) {
+  return t < tp.S ? wave_of(t, tp.S, W) : W + (int)((t - tp.S) / tp.C);
 }
 
 // Waves that share the T tiles of a stream-mode call: the W launched, or
@@ -1002,58 +1034,74 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   // (sequences with nothing attended get their zero rows from the combine)
   if (T == 0) return;
   const int NG = effective_groups(T, a.n_waves / kWaves);
-  if (grp >= NG) return;
-  const long s_begin = (long)grp * T / NG;
-  const long s_end = (long)(grp + 1) * T / NG;
+  const TailPlan tp = tail_plan(T, a.dyn);
 
-  // the sequence holding s_begin: the last one whose first tile is <= s_begin
-  int b = 0;
-  {
-    int lo_b = 0, hi_b = a.B - 1;
-    while (lo_b < hi_b) {
-      const int mid = (lo_b + hi_b + 1) >> 1;
-      if ((long)KV * s_before[mid] <= s_begin) lo_b = mid;
-      else hi_b = mid - 1;
+  // tiles [s_begin, s_end) of the flattened sequence (slice sl), unit piece by
+  // unit piece
+  auto run_range = [&](long s_begin, long s_end, int sl) {
+    // the sequence holding s_begin: the last one whose first tile is <= s_begin
+    int b = 0;
+    {
+      int lo_b = 0, hi_b = a.B - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if ((long)KV * s_before[mid] <= s_begin) lo_b = mid;
+        else hi_b = mid - 1;
+      }
+      b = lo_b;
     }
-    b = lo_b;
-  }
-  int n = s_cnt[b];
-  int g, kk0;
-  {
-    const int rel = (int)(s_begin - (long)KV * s_before[b]);
-    g = rel / n;
-    kk0 = rel % n;
-  }
-
-  long t = s_begin;
-  while (t < s_end) {
-    // ---- one piece: tiles [k_begin, k_end) of unit (b, g), shared by the waves
-    const SeqRange sr = seq_range(s_len[b], position_cap(a.cap, a.ring), a.window);
-    const int k_begin = kk0;
-    const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
-    WaveState<KV, D, BF16> st;
-    accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin + wave, k_end, kWaves,
-                                              s_q[wave], s_rope,
-                                              SB > 0 ? s_pool + wave * SB : nullptr, st);
-    if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
-    // a whole unit writes o; a piece writes the work-group's partial to slot
-    // unit + grp (the merge ends on a barrier: its LDS rows may then be reused)
-    const size_t slot = (size_t)(b * KV + g) + grp;
-    merge_store_group<KV, D, BF16>(
-        st, s_acc, s_m, s_l,
-        k_begin == 0 && k_end == n ? a.o + ((size_t)b * kHeads + g * G) * ROW : nullptr,
-        a.ws_acc + slot * G * D, a.ws_ml + slot * G * 2);
-
-    // ---- next unit (skipping sequences with nothing attended)
-    t += k_end - k_begin;
-    kk0 = 0;
-    if (++g == KV) {
-      g = 0;
-      do {
-        ++b;
-      } while (b < a.B && s_cnt[b] == 0);
+    int n = s_cnt[b];
+    int g, kk0;
+    {
+      const int rel = (int)(s_begin - (long)KV * s_before[b]);
+      g = rel / n;
+      kk0 = rel % n;
     }
-    if (t < s_end) n = s_cnt[b];
+
+    long t = s_begin;
+    while (t < s_end) {
+      // ---- one piece: tiles [k_begin, k_end) of unit (b, g), shared by the waves
+      const SeqRange sr = seq_range(s_len[b], position_cap(a.cap, a.ring), a.window);
+      const int k_begin = kk0;
+      const int k_end = (int)min((long)n, (long)k_begin + (s_end - t));
+      WaveState<KV, D, BF16> st;
+      accumulate_tiles<KV, D, PAGED, BF16, KFV>(a, b, g, sr, k_begin + wave, k_end, kWaves,
+                                                s_q[wave], s_rope,
+                                                SB > 0 ? s_pool + wave * SB : nullptr, st);
+      if constexpr (SB > 0) __syncthreads();  // the tiles are dead before s_acc is written
+      // a whole unit writes o; a piece writes the work-group's partial to slot
+      // unit + sl (the merge ends on a barrier: its LDS rows may then be reused)
+      const size_t slot = (size_t)(b * KV + g) + sl;
+      merge_store_group<KV, D, BF16>(
+          st, s_acc, s_m, s_l,
+          k_begin == 0 && k_end == n ? a.o + ((size_t)b * kHeads + g * G) * ROW : nullptr,
+          a.ws_acc + slot * G * D, a.ws_ml + slot * G * 2);
+
+      // ---- next unit (skipping sequences with nothing attended)
+      t += k_end - k_begin;
+      kk0 = 0;
+      if (++g == KV) {
+        g = 0;
+        do {
+          ++b;
+        } while (b < a.B && s_cnt[b] == 0);
+      }
+      if (t < s_end) n = s_cnt[b];
+    }
+  };
+  if (grp < NG) run_range((long)grp * tp.S / NG, (long)(grp + 1) * tp.S / NG, grp);
+  if (tp.nch > 0) {
+    // the dynamic tail: chunks from the counter until none is left (one lane
+    // takes the ticket; a value outside [0, nch) ends the loop)
+    __shared__ int s_chunk;
+    for (;;) {
+      __syncthreads();  // every wave has read the last ticket
+      if (threadIdx.x == 0) s_chunk = atomicAdd(a.counter, 1);
+      __syncthreads();
+      const int c = s_chunk;
+      if (c < 0 || c >= tp.nch) break;
+      run_range(tp.S + (long)c * tp.C, tp.S + (long)(c + 1) * tp.C, NG + c);
+    }
   }
 }
 
@@ -1065,6 +1113,7 @@ struct CombineArgs {
   int32_t B;
   int32_t n_waves;  // stream mode: the main kernel's waves; group mode: its work-groups
   int32_t groups;   // nonzero in group mode (slices per work-group, not per wave)
+  int32_t dyn;      // group mode: the main kernel's dyn (its tail_plan)
 };
 
 // One work-group of CW waves (8, or 4 when that many work-groups would not
@@ -1157,8 +1206,9 @@ __global__ __launch_bounds__(64 * CW) void gqa_combine_kernel(CombineArgs a) {
   }
   const long s0 = P0 + (long)g * n;
   const int W = a.groups ? effective_groups(T, a.n_waves) : effective_waves(T, a.n_waves);
-  const int wf = wave_of(s0, T, W);
-  const int wl = wave_of(s0 + n - 1, T, W);
+  const TailPlan tp = tail_plan(T, a.groups ? a.dyn : 0);
+  const int wf = slice_of(s0, tp, W);
+  const int wl = slice_of(s0 + n - 1, tp, W);
   if (wf == wl) return;  // written by the wave that held the whole unit
   const int ns = wl - wf + 1;
   const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + ((size_t)unit + wf) * G + hh;
@@ -1166,14 +1216,14 @@ __global__ __launch_bounds__(64 * CW) void gqa_combine_kernel(CombineArgs a) {
   const size_t sstride = (size_t)G * D;
   // waves between wf and wl whose slices are empty (more waves than tiles)
   // wrote nothing: their slots are skipped.  With at least as many tiles as
-  // waves every slice holds a tile; otherwise slice w = [wT/W, (w+1)T/W) is
-  // tested with double divisions, exact here: (w+1)T < 2^53 is exact, the
+  // waves every slice holds a tile; otherwise slice w = [wS/W, (w+1)S/W) is
+  // tested with double divisions, exact here: (w+1)S < 2^53 is exact, the
   // quotient is correctly rounded, and a quotient that is not an integer lies
-  // at least 1/W from one
-  const bool all_hold = T >= W;
-  const double Td = (double)T, Wd = (double)W;
+  // at least 1/W from one.  Every chunk of a dynamic tail holds C tiles.
+  const bool all_hold = tp.S >= W;
+  const double Td = (double)tp.S, Wd = (double)W;
   auto holds = [&](int s) {
-    if (all_hold) return true;
+    if (all_hold || wf + s >= W) return true;
     const double w = (double)(wf + s);
     return floor((w + 1.0) * Td / Wd) > floor(w * Td / Wd);
   };
@@ -1434,6 +1484,11 @@ __global__ __launch_bounds__(kThreads) void gqa_append_kernel(AppendArgs a) {
 
 constexpr int kProbeUnroll = 8;
 
+// the dynamic tail's chunk counter to zero (lane 0 of one wave)
+__global__ __launch_bounds__(64) void gqa_zero_counter_kernel(int32_t* counter) {
+  if (threadIdx.x == 0) *counter = 0;
+}
+
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* p, size_t n, unsigned* sink) {
   const size_t lane = threadIdx.x & 63;
   const size_t wave = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6;
@@ -1509,9 +1564,10 @@ inline bool unit_mode_fits(int units, int tiles_max, int D) {
 }
 
 struct Plan {
-  int mode;  // GQA_MODE_UNIT or GQA_MODE_STREAM
+  int mode;  // GQA_MODE_UNIT, GQA_MODE_STREAM or GQA_MODE_GROUP
   int waves, slots;
-  size_t prefix, ml, acc, total;
+  bool dyn;  // group mode with a dynamic tail (its counter zeroed before the launch)
+  size_t prefix, counter, ml, acc, total;
 };
 
 // window: attended positions per sequence (0 = every position below L)
@@ -1548,8 +1604,13 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   P->mode = mode;
   P->waves = vi.waves;
   P->slots = units + (mode == GQA_MODE_GROUP ? vi.waves / kWaves : vi.waves);
+  // a dynamic tail when the call may hold enough tiles (tail_plan decides on
+  // the actual count); its chunks add up to kDynMaxChunks slots
+  P->dyn = mode == GQA_MODE_GROUP && (long)units * tiles_max >= kDynMinTiles;
+  if (P->dyn) P->slots += kDynMaxChunks;
   P->prefix = 0;
-  P->ml = align256((size_t)(B + 1) * sizeof(int32_t));
+  P->counter = (size_t)(B + 1) * sizeof(int32_t);
+  P->ml = align256(P->counter + sizeof(int32_t));
   P->acc = P->ml + align256((size_t)P->slots * G * 2 * sizeof(float));
   P->total = P->acc + (size_t)P->slots * G * vi.D * sizeof(float);
   return GQA_OK;
@@ -1741,6 +1802,14 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
       !unit_mode && variant == GQA_SLIDING && !bf16 ? plan.waves / 2 : plan.waves;
   ka.n_waves = launch_waves;
   ka.ring = ring;
+  ka.dyn = plan.dyn ? 1 : 0;
+  ka.counter = plan.dyn ? reinterpret_cast<int32_t*>(ws + plan.counter) : nullptr;
+  // the dynamic tail's counter starts at zero (a kernel, not a memset, so that
+  // the call can be captured into a graph)
+  if (plan.dyn) {
+    hipLaunchKernelGGL(gqa_zero_counter_kernel, dim3(1), dim3(64), 0, stream, ka.counter);
+    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  }
 
   MainFn main_fn = variant == GQA_SLIDING ? pick_main<16, 256, false>(plan.mode, paged, bf16)
                    : kfv                   ? pick_main<4, 512, true>(plan.mode, paged, bf16)
@@ -1761,6 +1830,7 @@ int run(int variant, int window, bool paged, const void* q, const void* k, const
   ca.B = B;
   ca.n_waves = group_mode ? launch_waves / kWaves : launch_waves;
   ca.groups = group_mode ? 1 : 0;
+  ca.dyn = ka.dyn;
   const int ds = variant == GQA_SLIDING ? combine_parts<256>(B) : combine_parts<512>(B);
   const int cw = combine_waves(B * kHeads * ds);
   CombineFn comb =

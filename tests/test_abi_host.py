@@ -73,12 +73,15 @@ def test_plan_and_workspace(lib, variant, B, cap):
         assert ws == 0
     else:
         # split units: wave slices (stream mode) on the sliding geometry, work-group
-        # slices (group mode) on the global one; slot u + w for every (unit, slice)
+        # slices (group mode) on the global one; slot u + w for every (unit, slice),
+        # and in group mode over at least 2^19 tiles the dynamic tail's chunks
+        # (up to 768 more slices) and its counter
         assert plan["mode"] == ("stream" if variant == "sliding" else "group")
         assert plan["waves"] == (2048 if variant == "sliding" else 1024)
         slices = plan["waves"] if variant == "sliding" else plan["waves"] // 4
-        assert plan["slots"] == B * KV + slices
-        assert ws >= (B + 1) * 4 + plan["slots"] * G * (D + 2) * 4
+        dyn = variant == "global" and units * tiles >= 1 << 19
+        assert plan["slots"] == B * KV + slices + (768 if dyn else 0)
+        assert ws >= (B + 1) * 4 + (4 if dyn else 0) + plan["slots"] * G * (D + 2) * 4
 
 
 def test_plan_modes_of_the_workloads(lib):
@@ -86,6 +89,41 @@ def test_plan_modes_of_the_workloads(lib):
     assert gqa.gqa_decode_plan("global", 32, 131072)["mode"] == "group"
     assert gqa.gqa_decode_plan("global", 1, 262144)["mode"] == "group"
     assert gqa.gqa_decode_plan("sliding", 4, 2048)["mode"] == "stream"
+
+
+def tail_plan(T, dyn):
+    """The group partition's dynamic tail, as the kernels compute it: static
+    slices over [0, S), then nch chunks of C tiles."""
+    if not dyn or T < 1 << 19:
+        return T, 1, 0
+    Td = T // 12
+    C = max(128, -(-Td // 768))
+    nch = Td // C
+    return T - nch * C, C, nch
+
+
+def test_dynamic_tail_partitions_exactly():
+    # static slices [w*S//W, (w+1)*S//W) and chunks [S + c*C, S + (c+1)*C) cover
+    # [0, T) once; slice_of(t) names the slice or chunk holding t; at most 768
+    # chunks (the slots the plan adds) of at least 128 tiles
+    import random
+    rnd = random.Random(7)
+    for _ in range(300):
+        T = rnd.choice([(1 << 19) - 1, 1 << 19, 600_000, 1_221_000, 16_777_216, rnd.randint(1, 4_000_000)])
+        W = rnd.choice([64, 256])
+        S, C, nch = tail_plan(T, True)
+        assert S + nch * C == T and nch <= 768
+        if T < 1 << 19:
+            assert (S, nch) == (T, 0)
+            continue
+        assert C >= 128 and nch >= 1 and S >= W
+        for t in sorted({0, S - 1, S, T - 1} | {rnd.randrange(T) for _ in range(50)}):
+            sl = ((t + 1) * W - 1) // S if t < S else W + (t - S) // C
+            if sl < W:
+                assert sl * S // W <= t < (sl + 1) * S // W
+            else:
+                c = sl - W
+                assert 0 <= c < nch and S + c * C <= t < S + (c + 1) * C
 
 
 def test_slice_arithmetic_partitions_exactly():
