@@ -19,8 +19,8 @@ namespace {
 // Work: the query rows of one (sequence, kv head g) form T_b*G columns
 // (token-major, the G heads of a token adjacent); a wave takes 16 of them, a
 // work-group 64 or 128.  The work-group walks the union of its columns' key
-// ranges in steps of PT positions (32 for bf16, two 16-key MFMA halves; 16
-// for f32): each K/V step is fetched once with coalesced 16-byte loads into a
+// ranges in steps of PT positions (bf16: 32, two 16-key MFMA halves, or 64 on
+// the sliding layer; f32: 16): each K/V step is fetched once with coalesced 16-byte loads into a
 // double-buffered LDS tile with padded rows (operand reads free of bank
 // conflicts, every operand address a lane base plus an immediate), which all
 // waves use with every MFMA column masked to its own range.  bf16 P@V runs on 16x16x32 MFMAs over both halves
@@ -69,9 +69,14 @@ template <int KV, bool BF16>
 constexpr int prefill_waves() {
   return BF16 ? 8 : 4;
 }
+// The bf16 sliding layer takes 64 keys per step: each barrier, softmax
+// reduction and rescale test then serves twice the MFMA work (measured 1%
+// faster, 752-755 us against 761-767 on 8 x 2048 tokens after 4096); its
+// double buffer (139 KB) still fits one work-group per CU.  The global
+// layer's rows are twice as long and keep 32.
 template <int KV, bool BF16>
 constexpr int prefill_step() {
-  return BF16 ? 32 : 16;
+  return BF16 ? (KV == 16 ? 64 : 32) : 16;
 }
 
 // query columns per work-group
@@ -322,7 +327,17 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
       // compiler copy the argument block to scratch memory)
       auto half_ptr = [&](int which, int h) -> const char* {
         if (PAGED && !((okbits >> h) & 1)) return zero_page() + (size_t)g * ROW;
-        return (which ? v_base : k_base) + base[h];
+        // selects on the bits of h (a runtime index into base[] would put the
+        // array in scratch memory)
+        size_t off = base[0];
+        if constexpr (NH == 2) {
+          off = (h & 1) ? base[1] : base[0];
+        } else if constexpr (NH == 4) {
+          const size_t lo = (h & 1) ? base[1] : base[0];
+          const size_t hi = (h & 1) ? base[3] : base[2];
+          off = (h & 2) ? hi : lo;
+        }
+        return (which ? v_base : k_base) + off;
       };
       if constexpr (DMA) {
         // LDS-DMA through buffer descriptors, one per K/V and 16-row half of
@@ -386,7 +401,7 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
           const int rel = min(max(pos0 + row, range_lo), range_hi) - pos0;  // in [0, PT)
           const int h = rel >> 4;
           const size_t off = (size_t)(rel & 15) * POS + c * 16;
-          ld[u] = load16(half_ptr(which, NH == 1 ? 0 : (h ? NH - 1 : 0)) + off);
+          ld[u] = load16(half_ptr(which, h) + off);
         }
       }
     };
@@ -562,33 +577,42 @@ __global__ __launch_bounds__((64 * prefill_waves<KV, BF16>()), (prefill_waves_pe
             for (int i = 0; i < 4; ++i) p[cb][h][i] = exp2_fast(fmaf(z[cb][h][i], kLog2e, -m_log));
         }
         if constexpr (BF16) {
-          // P^T operands: k-slots 8j+e <-> keys 4j+e (half 0, e < 4), 16+4j+e-4 (half 1)
-          u32x4 pt[CB];
+          // P^T operands of each 32-key pair of halves hp (halves 2hp, 2hp+1):
+          // k-slots 8j+e <-> keys 4j+e (e < 4), 16+4j+e-4 (e >= 4)
+          constexpr int NP = NH / 2;
+          u32x4 pt[CB][NP];
           const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              pt[cb][2 * h] = bf16_pack2(p[cb][h][0], p[cb][h][1]);
-              pt[cb][2 * h + 1] = bf16_pack2(p[cb][h][2], p[cb][h][3]);
+            for (int hp = 0; hp < NP; ++hp) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                pt[cb][hp][2 * h] = bf16_pack2(p[cb][2 * hp + h][0], p[cb][2 * hp + h][1]);
+                pt[cb][hp][2 * h + 1] = bf16_pack2(p[cb][2 * hp + h][2], p[cb][2 * hp + h][3]);
+              }
+              // the column sums of the bf16 weights the P@V MFMAs use
+              lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pt[cb][hp]),
+                  lsum[cb], 0, 0, 0);
             }
-            // the column sums of the bf16 weights the P@V MFMAs use
-            lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pt[cb]), lsum[cb], 0,
-                0, 0);
           }
 #pragma unroll
           for (int t = 0; t < D / 16; ++t) {
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vt + 32 * t));
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vt + 16 * RSV + 32 * t));
-            const bf16x8 vop =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-              st[cb].acc[t / E][t % E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  vop, __builtin_bit_cast(bf16x8, pt[cb]), st[cb].acc[t / E][t % E], 0, 0, 0);
+            for (int hp = 0; hp < NP; ++hp) {
+              const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(vt + 32 * hp * RSV + 32 * t));
+              const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(vt + (32 * hp + 16) * RSV + 32 * t));
+              const bf16x8 vop = __builtin_bit_cast(
+                  bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+              for (int cb = 0; cb < CB; ++cb)
+                st[cb].acc[t / E][t % E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    vop, __builtin_bit_cast(bf16x8, pt[cb][hp]), st[cb].acc[t / E][t % E], 0, 0,
+                    0);
+            }
           }
         } else {
 #pragma unroll
