@@ -1563,6 +1563,10 @@ inline bool unit_mode_fits(int units, int tiles_max, int D) {
          (units >= 256 && tiles_max <= 128) || (D == 256 && units >= 128 && tiles_max <= 65);
 }
 
+// tiles (over all units, at the capacity) up to which a sliding call takes
+// group mode
+constexpr long kGroupSmallTiles = 2048;
+
 struct Plan {
   int mode;  // GQA_MODE_UNIT, GQA_MODE_STREAM or GQA_MODE_GROUP
   int waves, slots;
@@ -1591,9 +1595,14 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   // the sliding one (group mode, same box: global B=4 25.9 against 28.4 us,
   // B=1 320 against 327, B=32 and the values-only call equal; sliding bf16
   // B=1 equal, sliding f32 B=4 34.0 against 31.0)
+  // A tiny sliding call (at most kGroupSmallTiles tiles in all, e.g. one
+  // sequence's window) is latency-bound: group mode's LDS merge leaves a
+  // quarter of the partials for the combine (one sequence of 262,144
+  // positions, graph replay on one box: 11.45 against 11.95 us per call).
+  const bool tiny = (long)units * tiles_max <= kGroupSmallTiles;
   int mode = unit_mode_fits(units, tiles_max, vi.D)
                  ? GQA_MODE_UNIT
-                 : (variant == GQA_GLOBAL ? GQA_MODE_GROUP : GQA_MODE_STREAM);
+                 : (variant == GQA_GLOBAL || tiny ? GQA_MODE_GROUP : GQA_MODE_STREAM);
   if (g_force_mode >= 0) mode = g_force_mode;
   if (mode == GQA_MODE_UNIT) {
     P->mode = GQA_MODE_UNIT;

@@ -323,13 +323,16 @@ enum { GQA_MODE_UNIT = 0, GQA_MODE_STREAM = 1, GQA_MODE_GROUP = 2 };
  *   of at most 320 tiles of 16 positions, 256 of at most 128, or on the
  *   sliding geometry 128 of at most 65); no workspace; *n_waves = 4 * units,
  *   *n_slots = 0.
- * GQA_MODE_STREAM: *n_waves persistent waves each take an equal share of all
- *   tiles, partials of units shared by several waves go to *n_slots workspace
- *   slots, and a combine kernel merges them.
- * GQA_MODE_GROUP: *n_waves / 4 work-groups each take an equal share of all
- *   tiles (their four waves share each unit piece and merge it in LDS);
- *   partials of units shared by several work-groups go to *n_slots workspace
- *   slots, and the combine kernel merges them.
+ * GQA_MODE_STREAM (the sliding geometry's other calls): *n_waves persistent
+ *   waves each take an equal share of all tiles, partials of units shared by
+ *   several waves go to *n_slots workspace slots, and a combine kernel merges
+ *   them.
+ * GQA_MODE_GROUP (the global geometry's other calls, and sliding calls of at
+ *   most 2048 tiles of 16 positions over all units at the capacity):
+ *   *n_waves / 4 work-groups each take an equal share of all tiles (their four
+ *   waves share each unit piece and merge it in LDS); partials of units shared
+ *   by several work-groups go to *n_slots workspace slots, and the combine
+ *   kernel merges them.
  * Returns GQA_OK or GQA_ERR_SHAPE / GQA_ERR_DTYPE. */
 int gqa_decode_plan(int32_t variant, int32_t B, int32_t capacity, int32_t* mode,
                     int32_t* n_waves, int32_t* n_slots);

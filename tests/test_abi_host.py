@@ -73,12 +73,14 @@ def test_plan_and_workspace(lib, variant, B, cap):
         assert ws == 0
     else:
         # split units: wave slices (stream mode) on the sliding geometry, work-group
-        # slices (group mode) on the global one; slot u + w for every (unit, slice),
-        # and in group mode over at least 2^19 tiles the dynamic tail's chunks
-        # (up to 768 more slices) and its counter
-        assert plan["mode"] == ("stream" if variant == "sliding" else "group")
+        # slices (group mode) on the global one and on tiny sliding calls (at most
+        # 2048 tiles in all); slot u + w for every (unit, slice), and in group mode
+        # over at least 2^19 tiles the dynamic tail's chunks (up to 768 more
+        # slices) and its counter
+        group = variant == "global" or units * tiles <= 2048
+        assert plan["mode"] == ("group" if group else "stream")
         assert plan["waves"] == (2048 if variant == "sliding" else 1024)
-        slices = plan["waves"] if variant == "sliding" else plan["waves"] // 4
+        slices = plan["waves"] // 4 if group else plan["waves"]
         dyn = variant == "global" and units * tiles >= 1 << 19
         assert plan["slots"] == B * KV + slices + (768 if dyn else 0)
         assert ws >= (B + 1) * 4 + (4 if dyn else 0) + plan["slots"] * G * (D + 2) * 4
@@ -89,6 +91,7 @@ def test_plan_modes_of_the_workloads(lib):
     assert gqa.gqa_decode_plan("global", 32, 131072)["mode"] == "group"
     assert gqa.gqa_decode_plan("global", 1, 262144)["mode"] == "group"
     assert gqa.gqa_decode_plan("sliding", 4, 2048)["mode"] == "stream"
+    assert gqa.gqa_decode_plan("sliding", 1, 262144)["mode"] == "group"
 
 
 def tail_plan(T, dyn):
