@@ -60,7 +60,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_slidingdecodegqa_amd", "c
 SECTION_WARMUP = 10
 FLUSH_BYTES = 2 << 30   # a read of this many bytes evicts L2 and the 256 MB MALL
 SINGLE_CALLS = 50       # flushed single calls per workload (median reported)
-CPU_SHARE = 16          # host threads the GPU machine allots to one GPU
+CPU_SHARE = 16          # host threads allotted to one GPU on the measuring machine
 
 
 def log(msg):
@@ -144,7 +144,7 @@ def read_trace(key: str = "global_main"):
 
 
 def box_name() -> str:
-    """The GPU machine: host name and the device's UUID (PCI bus id without one)."""
+    """The machine: host name and the device's UUID (PCI bus id without one)."""
     try:
         import torch
         props = torch.cuda.get_device_properties(0)
