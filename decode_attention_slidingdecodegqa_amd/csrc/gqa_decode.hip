@@ -1592,9 +1592,9 @@ int make_plan(int variant, int B, int cap, int window, Plan* P) {
   const int units = B * vi.KV;
   *P = Plan{};
   // split units: work-group slices on the global geometry, wave slices on
-  // the sliding one (group mode, same machine: global B=4 25.9 against 28.4 us,
-  // B=1 320 against 327, B=32 and the values-only call equal; sliding bf16
-  // B=1 equal, sliding f32 B=4 34.0 against 31.0)
+  // the sliding one (group mode against stream mode, back-to-back calls on one
+  // machine: global B=4 25.9 against 28.4 us, B=1 320 against 327, B=32 and
+  // the values-only call equal; sliding f32 B=4 34.0 against 31.0)
   // A tiny sliding call (at most kGroupSmallTiles tiles in all, e.g. one
   // sequence's window) is latency-bound: group mode's LDS merge leaves a
   // quarter of the partials for the combine (one sequence of 262,144
