@@ -49,8 +49,9 @@
  * position.  Device behaviour outside them is memory-safe: seq_lens is
  * clamped to the capacity, seq_lens <= 0 gives a zero output row, a page id
  * outside [0, num_pages) is never dereferenced: its positions are dropped
- * from the softmax (the kernels read page 0 in its place and discard those
- * rows by selection, so nothing page 0 holds, NaN included, reaches o), and
+ * from the softmax (the kernels read a zero page the library holds in its
+ * place and set those positions' logits to -inf, so no pool byte behind an
+ * invalid id is read and nothing reaches o from it, NaN included), and
  * no K/V byte outside the attended range, and no block-table entry of a
  * page without an attended position, is ever read.
  *
@@ -255,8 +256,9 @@ int gqa_append_global_k_eq_v_paged(const void* q_raw, const void* k_raw, const v
  * T_b <= seq_lens[b] <= capacity, block-table entries of the attended pages
  * in [0, num_pages).  Rows whose position would be negative are zero;
  * seq_lens is clamped to the capacity; a page id outside the pool drops its
- * positions as in the decode calls (page 0 is read in its place and its
- * value rows are zeroed before P@V).  Softmax in fp32, P rounded to bf16 for bf16 inputs. */
+ * positions as in the decode calls (the library's zero page is read in its
+ * place and its logits are set to -inf).  Softmax in fp32, P rounded to bf16
+ * for bf16 inputs. */
 int gqa_prefill_sliding(const void* q, const void* k, const void* v, const int32_t* cu_q,
                         const int32_t* seq_lens, void* o, int32_t B, int32_t N, int32_t S_max,
                         int32_t dtype, void* stream);
