@@ -163,11 +163,12 @@ struct RopeLds {
 
 // The per-wave LDS tile of the staged (bf16 keys-from-values) path: 16 rows of
 // 512 bf16 values, unpadded, chunk c of row r stored at chunk c ^ f(r) with
-// f(r) = 4(r % 4) + 2((r / 4) % 2).  gfx950 serves a 16-byte-per-lane LDS
-// read in groups of 16 lanes taking rows r = 0..7 of one 16-lane quarter and
-// r = 8..15 of the next: the key-operand reads (row r, chunk 4c + j) then
-// split by parity and the value-operand reads (rows 4j + i, chunk r + 16 blk)
-// by bit 3, so neither has bank conflicts (a 16-byte row pad halves both).
+// f(r) = 4(r % 4) + 2((r / 4) % 2).  It serves the value operand; the key
+// operand comes from the fetch registers, whose rotated chunks are rebuilt in
+// place.  gfx950 serves a 16-byte-per-lane LDS read in groups of 16 lanes
+// taking rows r = 0..7 of one 16-lane quarter and r = 8..15 of the next: the
+// value-operand reads (rows 4j + i, chunk r + 16 blk) split by bit 3, so they
+// have no bank conflicts (a 16-byte row pad would halve the rate).
 template <bool KFV, bool BF16>
 constexpr bool kStaged = KFV && BF16;
 // bf16 stored keys: each tile's key rows are fetched whole (one 1 KiB load
@@ -181,9 +182,7 @@ template <bool KFV, bool BF16>
 constexpr bool kRowKeys = !KFV && BF16;
 constexpr int kStageRow = 512 * 2;
 __device__ __forceinline__ int stage_swz(int r) { return ((r & 3) << 2) | ((r & 4) >> 1); }
-constexpr int kStageTileBytes = kTile * kStageRow;
-// followed by the rebuilt key chunks: 4 slots x 64 lanes x 16 bytes
-constexpr int kStageBytes = kStageTileBytes + 4 * 64 * 16;
+constexpr int kStageBytes = kTile * kStageRow;
 // LDS bytes per wave of a main kernel: the keys-from-values tile, the
 // whole-row keys' tile (16 rows of ROW bytes), or none
 template <bool KFV, bool BF16, int ROW>
@@ -236,7 +235,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
                                                  WaveState<KV, D, BF16>& st) {
   static_assert(!KFV || (KV == 4 && D == 512), "keys from values: global layers only");
   // bf16 keys from values: each tile is fetched once (key layout) and staged
-  // in the wave's LDS buffer, from which both operand layouts are read
+  // in the wave's LDS buffer, from which the value operand is read
   constexpr bool STAGED = kStaged<KFV, BF16>;
   using Gm = Geo<KV, D, BF16>;
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
@@ -403,10 +402,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
 
   // Keys rebuilt from the value row in src: the lane's rotated pairs are
   // chunks t < TA (coordinates < 64) and their partners t + TP (+256).  The
-  // result goes back into src, or (staged) to slots t and TA + t of the
-  // wave's LDS area of rotated chunks (slot-major, 16 bytes per lane).
+  // result goes back into src.
   constexpr int TA = kRopePairs / (4 * E), TP = 256 / (4 * E);
-  u32x4* rot = STAGED ? reinterpret_cast<u32x4*>(stage + kStageTileBytes) : nullptr;
   // bf16: the lane's entries of M (its row r, its E pairs of chunks t < TA)
   // do not change from tile to tile, so they are read once here and kept in
   // registers, which the register allocator parks in AGPRs (1.8% faster than
@@ -482,13 +479,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
             kb[e] = __builtin_bit_cast(unsigned, vb[e]);
           }
         }
-        if constexpr (STAGED) {
-          rot[t * 64 + lane] = ka;
-          rot[(TA + t) * 64 + lane] = kb;
-        } else {
-          src[t] = ka;
-          src[t + TP] = kb;
-        }
+        src[t] = ka;
+        src[t + TP] = kb;
       }
     }
   };
@@ -496,11 +488,6 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   auto key_op = [&](int c) -> u32x4 {
     if constexpr (ROWK) {
       return *reinterpret_cast<const u32x4*>(stage + r * ROW + 16 * ((4 * c + j) ^ stage_swz(r)));
-    } else if constexpr (STAGED) {
-      if (c < TA) return rot[c * 64 + lane];
-      if (c >= TP && c < TP + TA) return rot[(TA + c - TP) * 64 + lane];
-      return *reinterpret_cast<const u32x4*>(stage + r * kStageRow +
-                                             16 * ((4 * c + j) ^ stage_swz(r)));
     } else {
       return kreg[c];
     }
@@ -532,17 +519,17 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     const TileAt nxt = more ? tile_at(it + 1) : cur;
 
     if constexpr (STAGED) {
-      // stage the fetched tile (row r, chunks 4t+j: 16-byte lanes, swizzled
-      // chunks), rebuild the rotated chunks from the registers, then refill
-      // the key registers with the next tile at once
+      // stage the fetched tile for the value operand (row r, chunks 4t+j:
+      // 16-byte lanes, swizzled chunks), then rebuild the rotated chunks in
+      // the registers, which QK^T reads as they are.  (The rebuilt chunks in
+      // an LDS area of their own, QK^T reading the key operand from LDS and
+      // the registers refilled at once: 1,608 against 1,595 us on the global
+      // B=32 paged call, same machine.)
       char* srow = stage + r * kStageRow;
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
         *reinterpret_cast<u32x4*>(srow + 16 * ((4 * c + j) ^ stage_swz(r))) = kreg[c];
       rebuild_keys(kreg);
-      if (more) load_k(nxt);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
     } else if constexpr (ROWK) {
       // this tile's key rows into the wave's LDS tile, then the registers
       // take the next tile's rows at once (fetched a whole QK^T earlier)
@@ -593,6 +580,11 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
       z = z0 + z1;
     }
     if constexpr (STAGED) {
+      // the key registers are free: fetch the next tile; the staging writes
+      // are complete before the value reads
+      if (more) load_k(nxt);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       // value operands: rows 4j+i (clamped as when fetched), chunks r+16*blk
 #pragma unroll
       for (int i = 0; i < 4; ++i)
