@@ -88,9 +88,53 @@ __device__ inline SeqRange seq_range(int L_raw, int cap, int window) {
   return s;
 }
 
+// floor(num / den) for 0 <= num < 2^40 and 0 < den < 2^27 (tile counts stay
+// below 2^26, slice counts below 2^12), in fp64: both operands are exact, the
+// quotient is correctly rounded, and a quotient that is not an integer lies at
+// least 1/den from one, far beyond its rounding error, so truncation gives the
+// integer quotient.  A 64-bit integer division expands into a long sequence
+// that would sit ahead of every work-group's first load.
+__device__ inline long floor_div(long num, long den) {
+  return (long)((double)num / (double)den);
+}
+
+// Cross-lane steps without LDS round trips (a ds_bpermute waits behind every
+// LDS access in flight): the lane swaps exchange lanes l and l ^ 16 (l ^ 32),
+// DPP row rotations move values within a 16-lane row.
+__device__ inline float max_lanes_xor16_32(float x) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+__device__ inline float sum_lanes_xor16_32(float x) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+// DPP row rotation by K lanes (row_ror:K) of a float
+template <int K>
+__device__ inline float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + K, 0xf, 0xf, false));
+}
+// the maximum over all 64 lanes, in every lane
+__device__ inline float max_wave(float x) {
+  x = max_lanes_xor16_32(x);
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  return fmaxf(x, row_ror<1>(x));
+}
+// DPP row shift right by K lanes (row_shr:K) of an int; lanes below K read 0
+template <int K>
+__device__ inline int row_shr(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x110 + K, 0xf, 0xf, true);
+}
+
 // Wave whose slice holds flattened tile t: slice w is [w*T/W, (w+1)*T/W).
 __device__ inline int wave_of(long t, long T, int W) {
-  return (int)(((t + 1) * W - 1) / T);
+  return (int)floor_div((t + 1) * W - 1, T);
 }
 
 // Dynamic tail of the group partition.  Equal static slices leave the XCDs
@@ -120,7 +164,7 @@ __host__ __device__ inline TailPlan tail_plan(long T, int dyn) {
 }
 // the slice holding flattened tile t (W static slices over [0, S), then the chunks)
 __device__ inline int slice_of(long t, const TailPlan& tp, int W) {
-  return t < tp.S ? wave_of(t, tp.S, W) : W + (int)((t - tp.S) / tp.C);
+  return t < tp.S ? wave_of(t, tp.S, W) : W + (int)(t - tp.S) / tp.C;
 }
 
 // Waves that share the T tiles of a stream-mode call: the W launched, or
@@ -675,8 +719,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     cur = nxt;
   }
   // the lane's share of l summed over the 4 lanes of its column
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
+  st.l = sum_lanes_xor16_32(st.l);
 }
 
 // Writes the wave's unnormalised O row of head r as fp32 (same ownership).
@@ -716,11 +759,19 @@ __device__ inline void tile_prefix(const KernelArgs& a, int* s_len, int* s_cnt, 
     }
   }
   const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  // inclusive scan over the lanes: within each 16-lane row by DPP row shifts
+  // (lanes below the shift read 0), then the totals of the rows below added
   int incl = lsum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
+  incl += row_shr<1>(incl);
+  incl += row_shr<2>(incl);
+  incl += row_shr<4>(incl);
+  incl += row_shr<8>(incl);
+  {
+    const int r0 = __builtin_amdgcn_readlane(incl, 15);
+    const int r1 = __builtin_amdgcn_readlane(incl, 31);
+    const int r2 = __builtin_amdgcn_readlane(incl, 47);
+    const int row = lane >> 4;
+    incl += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
   }
   int run_b = incl - lsum;
 #pragma unroll
@@ -768,8 +819,8 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
   // ---- this wave's slice [s_begin, s_end) of the flattened tiles
   const int W = effective_waves(T, a.n_waves);
   if (w >= W) return;
-  const long s_begin = (long)w * T / W;
-  const long s_end = (long)(w + 1) * T / W;
+  const long s_begin = floor_div((long)w * T, W);
+  const long s_end = floor_div((long)(w + 1) * T, W);
   if (s_begin >= s_end) return;
 
   // the sequence holding s_begin: the last one whose first tile is <= s_begin
@@ -1081,7 +1132,7 @@ __global__ __launch_bounds__(kThreads, (main_waves_per_simd<KV, BF16>())) void g
       if (t < s_end) n = s_cnt[b];
     }
   };
-  if (grp < NG) run_range((long)grp * tp.S / NG, (long)(grp + 1) * tp.S / NG, grp);
+  if (grp < NG) run_range(floor_div((long)grp * tp.S, NG), floor_div((long)(grp + 1) * tp.S, NG), grp);
   if (tp.nch > 0) {
     // the dynamic tail: chunks from the counter until none is left (one lane
     // takes the ticket; a value outside [0, nch) ends the loop)
@@ -1242,8 +1293,7 @@ __global__ __launch_bounds__(64 * CW) void gqa_combine_kernel(CombineArgs a) {
     const f32x2 y = ml[(size_t)s * G];
     if (y[1] > 0.f) M = fmaxf(M, y[0]);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  M = max_wave(M);
 
   float A[PER];
 #pragma unroll
