@@ -304,3 +304,30 @@ def test_product_path_does_not_touch_the_oracle():
                 src = open(os.path.join(dirpath, f)).read().lower()
                 assert "oracle" not in src, f
     assert "oracle" not in open(HEADER).read().lower()
+
+
+def test_slice_bounds_in_fp64_are_exact():
+    """The kernels take the slice bounds floor(w*T/W) and the slice of a tile,
+    floor(((t+1)*W - 1)/T), as fp64 divisions truncated to integers, for
+    numerators below 2^40 and denominators below 2^27 (tile counts stay below
+    2^26, slice counts below 2^12).  IEEE double division, which Python's float
+    shares, gives the integer quotient there: the operands are exact, the
+    quotient is correctly rounded, and a quotient that is not an integer lies
+    at least 1/den from one."""
+    import random
+    rng = random.Random(7)
+    cases = []
+    for den in (1, 2, 3, 12, 255, 256, 1023, 2048, (1 << 26) - 1, 1 << 26, (1 << 27) - 1):
+        top = ((1 << 40) - 1) // den * den
+        cases += [(0, den), (den - 1, den), (den, den), (den + 1, den), (top, den), (top - 1, den),
+                  ((1 << 40) - 1, den)]
+    cases += [(rng.randrange(1 << 40), rng.randrange(1, 1 << 27)) for _ in range(200000)]
+    # slice bounds as the kernels form them, at the largest tile and slice counts
+    for T in (1, 255, 1 << 20, (1 << 26) - 1, 1 << 26):
+        for W in (1, 256, 1023, 1024, 2048):
+            for w in (0, 1, W // 2, W - 1, W):
+                cases.append((w * T, W))
+            for t in (0, 1, T // 3, T - 1):
+                cases.append(((t + 1) * W - 1, T))
+    bad = [(n, d) for n, d in cases if int(float(n) / float(d)) != n // d]
+    assert not bad, bad[:5]
