@@ -88,8 +88,8 @@ __device__ inline SeqRange seq_range(int L_raw, int cap, int window) {
   return s;
 }
 
-// floor(num / den) for 0 <= num < 2^40 and 0 < den < 2^27 (tile counts stay
-// below 2^26, slice counts below 2^12), in fp64: both operands are exact, the
+// floor(num / den) for 0 <= num < 2^40 and 0 < den < 2^27 (tile counts are at
+// most 2^26, slice counts below 2^12), in fp64: both operands are exact, the
 // quotient is correctly rounded, and a quotient that is not an integer lies at
 // least 1/den from one, far beyond its rounding error, so truncation gives the
 // integer quotient.  A 64-bit integer division expands into a long sequence
