@@ -160,6 +160,20 @@ def test_mode_lengths_and_empty_sequences(variant):
 
 
 @pytest.mark.parametrize("variant", ["sliding", "global"])
+def test_mode_prefix_across_lane_rows(variant):
+    # the split kernels scan the sequences' tile counts four to a lane, in
+    # 16-lane rows: batches that end one sequence into the second, third and
+    # fourth row, with empty sequences among them
+    for B, seed in ((65, 615), (129, 616), (193, 617)):
+        lens = [int(x) for x in synth.draw_seq_lens(("uniform", 1, 300), B, seed)]
+        lens[3::7] = [0] * len(lens[3::7])
+        c = synth.make_case(variant, "bf16", B, 300, lens, seed=seed)
+        g = to_gpu(c)
+        err = max_err(to_f64(hip_run(g, o=_nan_out(g))), oracle_run(c))
+        assert err <= TOL["bf16"], (B, err)
+
+
+@pytest.mark.parametrize("variant", ["sliding", "global"])
 def test_mode_consecutive_calls_and_side_stream(variant):
     # calls of different shapes one after another on one stream, each into a
     # NaN output, then the same on a side stream
