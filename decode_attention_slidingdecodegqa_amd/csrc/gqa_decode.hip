@@ -207,12 +207,14 @@ struct RopeLds {
 
 // The per-wave LDS tile of the staged (bf16 keys-from-values) path: 16 rows of
 // 512 bf16 values, unpadded, chunk c of row r stored at chunk c ^ f(r) with
-// f(r) = 4(r % 4) + 2((r / 4) % 2).  It serves the value operand; the key
-// operand comes from the fetch registers, whose rotated chunks are rebuilt in
-// place.  gfx950 serves a 16-byte-per-lane LDS read in groups of 16 lanes
-// taking rows r = 0..7 of one 16-lane quarter and r = 8..15 of the next: the
-// value-operand reads (rows 4j + i, chunk r + 16 blk) split by bit 3, so they
-// have no bank conflicts (a 16-byte row pad would halve the rate).
+// f(r) = 4(r % 4) + 2((r / 4) % 2).  The rows arrive whole (as the stored
+// keys below) and both operand layouts are read back: the key operand into
+// the registers, where its rotated chunks are rebuilt, and the value operand.
+// gfx950 serves a 16-byte-per-lane LDS read in groups of 16 lanes taking rows
+// r = 0..7 of one 16-lane quarter and r = 8..15 of the next: the key-operand
+// reads (row r, chunk 4c + j) split by parity and the value-operand reads
+// (rows 4j + i, chunk r + 16 blk) by bit 3, so neither has bank conflicts (a
+// 16-byte row pad would halve the rate).
 template <bool KFV, bool BF16>
 constexpr bool kStaged = KFV && BF16;
 // bf16 stored keys: each tile's key rows are fetched whole (one 1 KiB load
@@ -220,8 +222,9 @@ constexpr bool kStaged = KFV && BF16;
 // and reach the MFMA operand layout (lane (r, j): row r, chunks 4c + j)
 // through a per-wave LDS tile of unpadded rows with the same chunk swizzle.
 // Fetched in the operand layout directly, every load instruction took 64
-// bytes of 16 rows: a plain read in that pattern measured 6.0 TB/s, whole
-// rows 7.37 TB/s, and the value rows' pattern (4 rows x 256 bytes) 7.1.
+// bytes of 16 rows, and consecutive lanes read different rows: a plain read
+// in that pattern measured 6.0 TB/s, whole rows 7.37 TB/s, and the value
+// rows' pattern (4 rows x 256 bytes) 7.1.
 template <bool KFV, bool BF16>
 constexpr bool kRowKeys = !KFV && BF16;
 constexpr int kStageRow = 512 * 2;
@@ -278,8 +281,8 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
                                                  int step, u32x4* myq, RopeLds* rl, char* stage,
                                                  WaveState<KV, D, BF16>& st) {
   static_assert(!KFV || (KV == 4 && D == 512), "keys from values: global layers only");
-  // bf16 keys from values: each tile is fetched once (key layout) and staged
-  // in the wave's LDS buffer, from which the value operand is read
+  // bf16 keys from values: each tile is fetched once, in whole rows, and
+  // staged in the wave's LDS buffer, from which both operands are read
   constexpr bool STAGED = kStaged<KFV, BF16>;
   using Gm = Geo<KV, D, BF16>;
   constexpr int G = Gm::G, E = Gm::E, ROW = Gm::ROW, NCH = Gm::NCH, KCH = Gm::KCH,
@@ -410,7 +413,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   u32x4 kreg[KCH];      // key row r of the tile, chunks 4t+j (ROWK: the raw rows)
   u32x4 vreg[4][VBLK];  // value rows 4j+i of the tile, chunks r+16*blk
   auto load_k = [&](const TileAt& ta) {
-    if constexpr (ROWK) {
+    if constexpr (ROWK || STAGED) {
       static_assert(KCH * 64 * 16 == kTile * ROW, "whole-row key fetch: one register per chunk");
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
@@ -426,7 +429,7 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
   // chunk p of row q at p ^ stage_swz(q)); written a whole row range per
   // instruction, so the writes are free of bank conflicts
   auto stage_keys = [&]() {
-    if constexpr (ROWK) {
+    if constexpr (ROWK || STAGED) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int q = krow_of(c);
@@ -563,16 +566,21 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
     const TileAt nxt = more ? tile_at(it + 1) : cur;
 
     if constexpr (STAGED) {
-      // stage the fetched tile for the value operand (row r, chunks 4t+j:
-      // 16-byte lanes, swizzled chunks), then rebuild the rotated chunks in
-      // the registers, which QK^T reads as they are.  (The rebuilt chunks in
-      // an LDS area of their own, QK^T reading the key operand from LDS and
-      // the registers refilled at once: 1,608 against 1,595 us on the global
-      // B=32 paged call, same machine.)
-      char* srow = stage + r * kStageRow;
+      // stage the fetched rows, read the key operand (row r, chunks 4c+j)
+      // back into the registers and rebuild its rotated chunks there; QK^T
+      // reads them as they are, and the registers take the next tile's rows
+      // after QK^T.  On the global B=32 paged call, same machine: 1,526-1,536
+      // us; the tile fetched in the key layout directly (no LDS round trip
+      // before the rebuild), 1,599-1,600; that fetch with the rebuilt chunks
+      // in an LDS area of their own, QK^T reading its keys from LDS and the
+      // registers refilled right after staging, 1,608.
+      stage_keys();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const char* srow = stage + r * kStageRow;
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        *reinterpret_cast<u32x4*>(srow + 16 * ((4 * c + j) ^ stage_swz(r))) = kreg[c];
+        kreg[c] = *reinterpret_cast<const u32x4*>(srow + 16 * ((4 * c + j) ^ stage_swz(r)));
       rebuild_keys(kreg);
     } else if constexpr (ROWK) {
       // this tile's key rows into the wave's LDS tile, then the registers
