@@ -281,6 +281,13 @@ __device__ __forceinline__ void accumulate_tiles(const KernelArgs& a, int b, int
                                                  int step, u32x4* myq, RopeLds* rl, char* stage,
                                                  WaveState<KV, D, BF16>& st) {
   static_assert(!KFV || (KV == 4 && D == 512), "keys from values: global layers only");
+  // wave-uniform in every caller, but derived from the lane's thread index or
+  // from LDS reads: taken through a scalar register so that the tile and row
+  // addressing below runs on the scalar unit instead of in every lane
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+  k_end = __builtin_amdgcn_readfirstlane(k_end);
   // bf16 keys from values: each tile is fetched once, in whole rows, and
   // staged in the wave's LDS buffer, from which both operands are read
   constexpr bool STAGED = kStaged<KFV, BF16>;
